@@ -1,0 +1,133 @@
+/*
+ * spgemm.h -- C ABI of the software-pipelined, tiled MFMA GEMM for MI355X (gfx950).
+ *
+ *   C[M,N] = epi( A[M,K] . B )       fp16 or bf16 inputs, fp32 accumulation,
+ *                                    fp16 / bf16 / fp32 output.
+ *
+ * The operation is the output-stationary tiled matrix product that the Mosaic
+ * GPU pipelining guide (Pallas) builds in "Example: matmul kernel on Hopper
+ * GPUs" ([M,K] @ [K,N], each output block owned by one program, K reduced by a
+ * pipelined sequential loop) and that the TileLang pipelined GEMM tutorial
+ * (chapter "pipeline and autotuning", matmul_auto) writes with B stored [N,K]
+ * and transpose_B=True.  The optional epilogue is the tanh approximation of
+ * GELU that the XLA:GPU emitters page fuses in its loop-emitter example and the
+ * Triton lecture notes write in their GeLU kernel:
+ *     gelu(x) = 0.5 x (1 + tanh(0.7978845608 (x + 0.044715 x^3))),
+ * applied to the fp32 accumulator before the output conversion.
+ *
+ * Conventions shared by every entry point:
+ *   - Matrices are dense and row-major.  A is [M,K] (leading dimension K).
+ *     B is [K,N] (GEMM_B_KN, leading dimension N) or [N,K] (GEMM_B_NK,
+ *     leading dimension K).  C is [M,N] (leading dimension N).
+ *   - A, B and C are device pointers owned by the caller; the library never
+ *     frees or retains them.  C must not overlap A or B (not checked).
+ *   - Out-of-range elements of partial tiles contribute exactly zero and are
+ *     never written: any M, N, K >= 0 is accepted.  M == 0 or N == 0 is a no-op;
+ *     K == 0 writes epi(0) = 0 everywhere.
+ *   - Errors are reported only through gemm_status; nothing aborts and no C++
+ *     exception crosses this interface.  Argument checks run before any HIP
+ *     call, so they behave the same on a machine without a GPU.
+ *   - Rounding to fp16/bf16 is to nearest, ties to even.
+ */
+#ifndef SPGEMM_H
+#define SPGEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_ARG = 1,   /* NULL handle/pointer, negative size, unknown enum, bad config */
+    GEMM_ERR_UNSUPPORTED = 2,   /* valid request this build cannot run (e.g. forced tile unknown) */
+    GEMM_ERR_OUT_OF_MEMORY = 3, /* host or device allocation failed */
+    GEMM_ERR_HIP = 4,           /* a HIP runtime call failed (no device, launch error, ...) */
+    GEMM_ERR_INTERNAL = 5
+} gemm_status;
+
+typedef enum { GEMM_F16 = 0, GEMM_BF16 = 1, GEMM_F32 = 2 /* output only */ } gemm_dtype;
+
+typedef enum {
+    GEMM_B_KN = 0, /* B row-major [K,N]  ("NN") */
+    GEMM_B_NK = 1  /* B row-major [N,K]  ("TN", transpose_B) */
+} gemm_b_layout;
+
+typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1 } gemm_epilogue;
+
+/* Tile configuration of the pipelined kernel.
+ *   block_m x block_n   output tile of one workgroup (128 or 256 each)
+ *   block_k             K extent of one pipeline stage (64)
+ *   stages              LDS ring depth S (1 = no overlap, the serial K loop of the
+ *                       TileLang tutorial's matmul_plain; 2..4 = loads of k-tile t+S-1
+ *                       in flight while k-tile t is multiplied)
+ *   wave_m x wave_n     output tile of one 64-lane wave (multiples of 32)
+ *   swizzle             1 = XOR-swizzled LDS layout, 0 = plain row layout (ablation)
+ *   group_m             tile-raster group height in tiles (L2 reuse); 0 = default
+ *   xcd_remap           1 = give each of the 8 XCDs a contiguous range of tiles
+ * The LDS a configuration needs is stages * (block_m + block_n) * block_k * 2 bytes
+ * (the shared-memory bound of the TileLang tutorial's shared_bytes()), at most 160 KiB. */
+typedef struct {
+    int32_t block_m, block_n, block_k;
+    int32_t stages;
+    int32_t wave_m, wave_n;
+    int32_t swizzle;
+    int32_t group_m;
+    int32_t xcd_remap;
+} gemm_tile_config;
+
+typedef struct gemm_plan* gemm_handle;
+
+/* Create a plan for one problem.  `force` == NULL picks a configuration from the
+ * shape (or the best one a previous gemm_autotune found for the same problem in
+ * this process); otherwise the forced configuration is used and must be one of
+ * gemm_list_configs() (group_m / xcd_remap may take any value >= 0 / {0,1}).
+ * Allocates host memory only; never synchronizes.
+ * Errors: INVALID_ARG (out NULL, M/N/K < 0, unknown dtype/layout/epilogue,
+ * in_dtype F32, malformed force), UNSUPPORTED (force not compiled in). */
+gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_dtype in_dtype,
+                        gemm_dtype out_dtype, gemm_b_layout b_layout, gemm_epilogue epilogue,
+                        const gemm_tile_config* force);
+
+/* Enqueue C = epi(A . B) on `stream` (0 = null stream).  Asynchronous: no
+ * allocation, no synchronization.  A, B, C are device pointers as described
+ * above.  Errors: INVALID_ARG (NULL handle, or NULL pointer with a non-empty
+ * operand), HIP (launch failure). */
+gemm_status gemm_run(gemm_handle h, const void* A, const void* B, void* C, hipStream_t stream);
+
+/* Release a plan.  NULL is a no-op. */
+gemm_status gemm_destroy(gemm_handle h);
+
+/* The configuration a plan will launch (a plan that falls back to the simple
+ * kernel for unaligned operands reports block_k = 0). */
+gemm_status gemm_get_config(gemm_handle h, gemm_tile_config* out);
+
+/* Time every compiled configuration that fits the plan's problem on the caller's
+ * buffers (C is overwritten), `reps` launches each after one warm-up, and make the
+ * fastest the plan's configuration; also remembered for later gemm_create calls
+ * with the same problem in this process.  Synchronizes `stream`.  best_us (may be
+ * NULL) receives the winner's mean time per launch in microseconds. */
+gemm_status gemm_autotune(gemm_handle h, const void* A, const void* B, void* C,
+                          hipStream_t stream, int reps, double* best_us);
+
+/* Static table of compiled configurations (valid for any dtype/layout). */
+int32_t gemm_num_configs(void);
+gemm_status gemm_list_config(int32_t index, gemm_tile_config* out);
+
+/* LDS bytes a configuration needs: stages * (block_m + block_n) * block_k * 2. */
+int64_t gemm_lds_bytes(const gemm_tile_config* cfg);
+
+/* Human-readable name of a status code (static storage). */
+const char* gemm_status_string(gemm_status s);
+
+/* Text of the last HIP error this thread's calls into the library saw (hipGetErrorString
+ * of the failing call), or "" if none.  Valid until the thread's next library call. */
+const char* gemm_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPGEMM_H */

@@ -1,0 +1,353 @@
+// C ABI of the software-pipelined tiled GEMM (declared in include/spgemm.h).
+//
+// Host side: argument validation (before any HIP call), the table of compiled
+// tile configurations, the shape heuristic, the autotuner (the Pallas guide
+// recommends autotuning max_concurrent_steps; the TileLang tutorial's chapter
+// pairs pipelining with autotuning and bounds each candidate's shared memory by
+// stages * (block_M + block_N) * block_K * bytes), and the launch.
+#include "spgemm.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <new>
+#include <tuple>
+#include <vector>
+
+#include "gemm_kernels.hpp"
+
+using spg::KArgs;
+
+namespace {
+
+typedef void (*launch_fn)(const KArgs&, dim3, hipStream_t);
+
+template <bool BF16, bool B_NK, int BM, int BN, int WM, int WN, int S, bool SWZ>
+void launch_pipelined(const KArgs& a, dim3 grid, hipStream_t st) {
+    using G = spg::Geom<BM, BN, WM, WN, S>;
+    hipLaunchKernelGGL((spg::pipelined_gemm<BF16, B_NK, BM, BN, WM, WN, S, SWZ>), grid,
+                       dim3(G::NT), 0, st, a);
+}
+
+template <bool BF16, bool B_NK>
+void launch_simple(const KArgs& a, dim3 grid, hipStream_t st) {
+    hipLaunchKernelGGL((spg::simple_gemm<BF16, B_NK>), grid, dim3(256), 0, st, a);
+}
+
+struct Variant {
+    gemm_tile_config cfg;
+    launch_fn fn[2][2];  // [bf16][b_nk]
+};
+
+#define SPG_VARIANT(BM, BN, WM, WN, S, SWZ)                                          \
+    Variant{{BM, BN, 64, S, WM, WN, SWZ, 0, 1},                                      \
+            {{launch_pipelined<false, false, BM, BN, WM, WN, S, (SWZ != 0)>,         \
+              launch_pipelined<false, true, BM, BN, WM, WN, S, (SWZ != 0)>},         \
+             {launch_pipelined<true, false, BM, BN, WM, WN, S, (SWZ != 0)>,          \
+              launch_pipelined<true, true, BM, BN, WM, WN, S, (SWZ != 0)>}}}
+
+// The compiled configurations.  LDS per workgroup = S * (BM + BN) * 64 * 2 B.
+const Variant kVariants[] = {
+    SPG_VARIANT(256, 256, 128, 128, 2, 1),  // 128 KiB
+    SPG_VARIANT(256, 128, 128, 64, 2, 1),   //  96 KiB
+    SPG_VARIANT(256, 128, 128, 64, 3, 1),   // 144 KiB
+    SPG_VARIANT(128, 256, 64, 128, 2, 1),   //  96 KiB
+    SPG_VARIANT(128, 256, 64, 128, 3, 1),   // 144 KiB
+    SPG_VARIANT(128, 128, 64, 64, 2, 1),    //  64 KiB
+    SPG_VARIANT(128, 128, 64, 64, 3, 1),    //  96 KiB
+    SPG_VARIANT(128, 128, 64, 64, 4, 1),    // 128 KiB
+    // ablations: no overlap (S = 1) and no swizzle
+    SPG_VARIANT(256, 256, 128, 128, 1, 1),  //  64 KiB
+    SPG_VARIANT(256, 256, 128, 128, 2, 0),  // 128 KiB
+    SPG_VARIANT(128, 128, 64, 64, 1, 1),    //  32 KiB
+};
+constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
+constexpr int kDefaultGroupM = 4;
+
+struct ProblemKey {
+    int64_t M, N, K;
+    int in, out, bl, epi;
+    bool operator<(const ProblemKey& o) const {
+        return std::tie(M, N, K, in, out, bl, epi) < std::tie(o.M, o.N, o.K, o.in, o.out, o.bl, o.epi);
+    }
+};
+
+thread_local char g_last_hip_error[256] = "";
+
+gemm_status hip_fail(hipError_t e) {
+    snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s (%d)", hipGetErrorString(e), (int)e);
+    return GEMM_ERR_HIP;
+}
+
+std::mutex g_tuned_mu;
+std::map<ProblemKey, gemm_tile_config> g_tuned;
+
+bool same_tile(const gemm_tile_config& a, const gemm_tile_config& b) {
+    return a.block_m == b.block_m && a.block_n == b.block_n && a.block_k == b.block_k &&
+           a.stages == b.stages && a.wave_m == b.wave_m && a.wave_n == b.wave_n &&
+           a.swizzle == b.swizzle;
+}
+
+const Variant* find_variant(const gemm_tile_config& c) {
+    for (const Variant& v : kVariants)
+        if (same_tile(v.cfg, c)) return &v;
+    return nullptr;
+}
+
+}  // namespace
+
+struct gemm_plan {
+    int64_t M, N, K;
+    gemm_dtype in, out;
+    gemm_b_layout bl;
+    gemm_epilogue epi;
+    bool simple;       // operands do not meet the pipelined kernel's alignment rules
+    const Variant* var;
+    gemm_tile_config cfg;
+};
+
+namespace {
+
+bool valid_dtype_in(int d) { return d == GEMM_F16 || d == GEMM_BF16; }
+bool valid_dtype_out(int d) { return d == GEMM_F16 || d == GEMM_BF16 || d == GEMM_F32; }
+
+// Shape conditions of the pipelined kernel: 16-B rows for the direct-to-LDS copies
+// and 32-bit buffer offsets.  Anything else runs on the simple kernel.
+bool pipelined_fits(int64_t M, int64_t N, int64_t K, gemm_b_layout bl) {
+    if (K <= 0 || M <= 0 || N <= 0) return false;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return false;
+    if (K % 8 != 0) return false;
+    const int64_t lim = (int64_t)1 << 31;
+    if (256 * K * 2 >= lim) return false;
+    if (bl == GEMM_B_KN) {
+        if (N % 8 != 0) return false;
+        if (K * N * 2 >= lim) return false;
+    }
+    return true;
+}
+
+gemm_tile_config heuristic(int64_t M, int64_t N) {
+    // Prefer the largest tile (least L2->LDS traffic per flop) that still gives
+    // every CU at least one tile; MI355X has 256 CUs.
+    auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    const int64_t cus = 256;
+    gemm_tile_config c;
+    if (tiles(256, 128) >= cus) c = kVariants[2].cfg;
+    else c = kVariants[6].cfg;
+    c.group_m = kDefaultGroupM;
+    c.xcd_remap = 1;
+    return c;
+}
+
+KArgs make_args(const gemm_plan* p, const void* A, const void* B, void* C, int bm, int bn) {
+    KArgs a;
+    a.A = (const uint16_t*)A;
+    a.B = (const uint16_t*)B;
+    a.C = C;
+    a.M = (int32_t)p->M;
+    a.N = (int32_t)p->N;
+    a.K = (int32_t)p->K;
+    a.tiles_m = (int32_t)((p->M + bm - 1) / bm);
+    a.tiles_n = (int32_t)((p->N + bn - 1) / bn);
+    a.group_m = p->cfg.group_m > 0 ? p->cfg.group_m : kDefaultGroupM;
+    a.xcd_remap = p->cfg.xcd_remap ? 1 : 0;
+    a.out_dtype = (int32_t)p->out;
+    a.epilogue = (int32_t)p->epi;
+    return a;
+}
+
+gemm_status launch_plan(const gemm_plan* p, const gemm_tile_config& cfg, const Variant* var,
+                        const void* A, const void* B, void* C, hipStream_t st) {
+    const bool bf = p->in == GEMM_BF16;
+    const bool nk = p->bl == GEMM_B_NK;
+    const bool aligned = ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0);
+    if (p->simple || !aligned || var == nullptr) {
+        gemm_plan q = *p;
+        q.cfg.group_m = 1;
+        KArgs a = make_args(&q, A, B, C, 64, 64);
+        dim3 grid((unsigned)a.tiles_n, (unsigned)a.tiles_m);
+        (bf ? (nk ? launch_simple<true, true> : launch_simple<true, false>)
+            : (nk ? launch_simple<false, true> : launch_simple<false, false>))(a, grid, st);
+    } else {
+        gemm_plan q = *p;
+        q.cfg = cfg;
+        KArgs a = make_args(&q, A, B, C, cfg.block_m, cfg.block_n);
+        dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
+        var->fn[bf ? 1 : 0][nk ? 1 : 0](a, grid, st);
+    }
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? GEMM_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gemm_status_string(gemm_status s) {
+    switch (s) {
+        case GEMM_OK: return "ok";
+        case GEMM_ERR_INVALID_ARG: return "invalid argument";
+        case GEMM_ERR_UNSUPPORTED: return "unsupported";
+        case GEMM_ERR_OUT_OF_MEMORY: return "out of memory";
+        case GEMM_ERR_HIP: return "HIP runtime error";
+        case GEMM_ERR_INTERNAL: return "internal error";
+    }
+    return "unknown status";
+}
+
+const char* gemm_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t gemm_num_configs(void) { return kNumVariants; }
+
+gemm_status gemm_list_config(int32_t index, gemm_tile_config* out) {
+    if (!out || index < 0 || index >= kNumVariants) return GEMM_ERR_INVALID_ARG;
+    *out = kVariants[index].cfg;
+    out->group_m = kDefaultGroupM;
+    return GEMM_OK;
+}
+
+int64_t gemm_lds_bytes(const gemm_tile_config* c) {
+    if (!c) return -1;
+    return (int64_t)c->stages * ((int64_t)c->block_m + c->block_n) * c->block_k * 2;
+}
+
+gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_dtype in_dtype,
+                        gemm_dtype out_dtype, gemm_b_layout b_layout, gemm_epilogue epilogue,
+                        const gemm_tile_config* force) {
+    if (!out) return GEMM_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
+    if (!valid_dtype_in((int)in_dtype) || !valid_dtype_out((int)out_dtype)) return GEMM_ERR_INVALID_ARG;
+    if (b_layout != GEMM_B_KN && b_layout != GEMM_B_NK) return GEMM_ERR_INVALID_ARG;
+    if (epilogue != GEMM_EPI_NONE && epilogue != GEMM_EPI_GELU_TANH) return GEMM_ERR_INVALID_ARG;
+
+    const Variant* var = nullptr;
+    gemm_tile_config cfg;
+    if (force) {
+        if (force->block_m <= 0 || force->block_n <= 0 || force->block_k <= 0 ||
+            force->stages <= 0 || force->wave_m <= 0 || force->wave_n <= 0 ||
+            force->group_m < 0 || (force->swizzle != 0 && force->swizzle != 1) ||
+            (force->xcd_remap != 0 && force->xcd_remap != 1))
+            return GEMM_ERR_INVALID_ARG;
+        if (gemm_lds_bytes(force) > 160 * 1024) return GEMM_ERR_UNSUPPORTED;
+        var = find_variant(*force);
+        if (!var) return GEMM_ERR_UNSUPPORTED;
+        cfg = *force;
+        if (cfg.group_m == 0) cfg.group_m = kDefaultGroupM;
+    } else {
+        bool have = false;
+        {
+            std::lock_guard<std::mutex> lk(g_tuned_mu);
+            auto it = g_tuned.find(ProblemKey{M, N, K, in_dtype, out_dtype, b_layout, epilogue});
+            if (it != g_tuned.end()) {
+                cfg = it->second;
+                have = true;
+            }
+        }
+        if (!have) cfg = heuristic(M, N);
+        var = find_variant(cfg);
+        if (!var) return GEMM_ERR_INTERNAL;
+    }
+    gemm_plan* p = new (std::nothrow) gemm_plan;
+    if (!p) return GEMM_ERR_OUT_OF_MEMORY;
+    p->M = M;
+    p->N = N;
+    p->K = K;
+    p->in = in_dtype;
+    p->out = out_dtype;
+    p->bl = b_layout;
+    p->epi = epilogue;
+    p->simple = !pipelined_fits(M, N, K, b_layout);
+    p->var = var;
+    p->cfg = cfg;
+    *out = p;
+    return GEMM_OK;
+}
+
+gemm_status gemm_destroy(gemm_handle h) {
+    delete h;
+    return GEMM_OK;
+}
+
+gemm_status gemm_get_config(gemm_handle h, gemm_tile_config* out) {
+    if (!h || !out) return GEMM_ERR_INVALID_ARG;
+    *out = h->cfg;
+    if (h->simple) {
+        *out = gemm_tile_config{64, 64, 0, 1, 64, 64, 0, 1, 0};
+    }
+    return GEMM_OK;
+}
+
+gemm_status gemm_run(gemm_handle h, const void* A, const void* B, void* C, hipStream_t stream) {
+    if (!h) return GEMM_ERR_INVALID_ARG;
+    if (h->M == 0 || h->N == 0) return GEMM_OK;
+    if (!C) return GEMM_ERR_INVALID_ARG;
+    if (h->K > 0 && (!A || !B)) return GEMM_ERR_INVALID_ARG;
+    return launch_plan(h, h->cfg, h->var, A, B, C, stream);
+}
+
+gemm_status gemm_autotune(gemm_handle h, const void* A, const void* B, void* C,
+                          hipStream_t stream, int reps, double* best_us) {
+    if (!h || reps <= 0) return GEMM_ERR_INVALID_ARG;
+    if (h->M == 0 || h->N == 0) return GEMM_OK;
+    if (!C || (h->K > 0 && (!A || !B))) return GEMM_ERR_INVALID_ARG;
+    if (h->simple) {
+        if (best_us) *best_us = -1.0;
+        return GEMM_OK;
+    }
+    hipEvent_t e0, e1;
+    hipError_t he = hipEventCreate(&e0);
+    if (he != hipSuccess) return hip_fail(he);
+    he = hipEventCreate(&e1);
+    if (he != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return hip_fail(he);
+    }
+    gemm_status st = GEMM_OK;
+    float best = -1.0f;
+    gemm_tile_config best_cfg = h->cfg;
+    const Variant* best_var = h->var;
+    const int groups[] = {4, 8, 16};
+    for (const Variant& v : kVariants) {
+        if (v.cfg.swizzle == 0 || v.cfg.stages == 1) continue;  // ablations are not candidates
+        for (int g : groups) {
+            gemm_tile_config c = v.cfg;
+            c.group_m = g;
+            c.xcd_remap = 1;
+            st = launch_plan(h, c, &v, A, B, C, stream);  // warm-up
+            if (st != GEMM_OK) break;
+            if ((he = hipEventRecord(e0, stream)) != hipSuccess) { st = hip_fail(he); break; }
+            for (int r = 0; r < reps && st == GEMM_OK; ++r) st = launch_plan(h, c, &v, A, B, C, stream);
+            if (st != GEMM_OK) break;
+            if ((he = hipEventRecord(e1, stream)) != hipSuccess) { st = hip_fail(he); break; }
+            if ((he = hipEventSynchronize(e1)) != hipSuccess) { st = hip_fail(he); break; }
+            float ms = 0.0f;
+            if ((he = hipEventElapsedTime(&ms, e0, e1)) != hipSuccess) { st = hip_fail(he); break; }
+            if (best < 0.0f || ms < best) {
+                best = ms;
+                best_cfg = c;
+                best_var = &v;
+            }
+        }
+        if (st != GEMM_OK) break;
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (st != GEMM_OK) return st;
+    h->cfg = best_cfg;
+    h->var = best_var;
+    {
+        std::lock_guard<std::mutex> lk(g_tuned_mu);
+        g_tuned[ProblemKey{h->M, h->N, h->K, h->in, h->out, h->bl, h->epi}] = best_cfg;
+    }
+    if (best_us) *best_us = best > 0 ? 1000.0 * best / reps : -1.0;
+    return GEMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,627 @@
+// Device code of the software-pipelined tiled GEMM for gfx950 (MI355X).
+//
+//   C[M,N] = epi( A[M,K] . B ),  A row-major [M,K]; B row-major [K,N] ("kn") or [N,K] ("nk").
+//
+// The method is the output-stationary tiling with a pipelined K loop that the
+// Mosaic GPU pipelining guide (Pallas) builds in "Example: matmul kernel on
+// Hopper GPUs" and that the TileLang pipelined GEMM tutorial writes as
+// T.Pipelined(ceildiv(K, block_K), num_stages): one workgroup owns a BM x BN
+// block of C, holds its fp32 accumulator in registers across the whole K loop,
+// and streams k-tiles of A and B through a ring of S shared-memory (LDS) slots
+// so that the copies of later k-tiles overlap the matrix-core work on the
+// current one.  What is specific to gfx950 here:
+//
+//  * Copies go straight from HBM/L2 to LDS with `buffer_load_dwordx4 ... lds`
+//    (16 B per lane, 1 KiB per wave instruction), so no VGPRs stage the tiles.
+//    A buffer resource per operand makes every access past the end of the
+//    matrix return zero, which is how partial tiles read "other = 0"
+//    (the masked loads of the Triton matmul in the Triton lecture notes).
+//  * Each ring slot is its own __shared__ array and the K loop is unrolled by
+//    S, so every slot index is a compile-time constant.  The compiler can then
+//    prove that the LDS reads of slot t%S do not alias the DMA into slot
+//    (t+S-1)%S and does not insert a full `s_waitcnt vmcnt(0)` before them;
+//    the kernel waits for exactly the k-tile it needs with `vmcnt(N)`.
+//  * Delayed release (the guide's delay_release): slot (t-1)%S is refilled
+//    only after the one barrier of iteration t, i.e. one iteration after its
+//    last use.  MFMA reads registers, not LDS, so a slot is free once every
+//    wave's LDS reads of it have returned, which the barrier guarantees.  One
+//    barrier per k-tile suffices.
+//  * LDS tiles are XOR-swizzled at 16-byte granularity (the "swizzling" the
+//    Triton notes give as the fix for bank conflicts, and the 128-byte swizzle
+//    of the Pallas example) so that the 64 lanes of an operand read hit
+//    distinct banks; the swizzle is applied by permuting the *global* chunk
+//    each lane fetches, because direct-to-LDS writes land at lane*16.
+//  * v_mfma_f32_32x32x16_{f16,bf16}; the B tile is the first MFMA operand and
+//    the A tile the second, so each lane's accumulator holds 4 consecutive
+//    output columns, which lets the epilogue pack 4 outputs per LDS write.
+//  * B stored [K,N] (N contiguous) is read with ds_read_b64_tr_b16, the
+//    gfx950 transposing LDS read, instead of being transposed in registers.
+//  * Epilogue: optional GELU on the fp32 accumulator, round-to-nearest-even
+//    conversion, staging through LDS (aliasing the drained ring), and 16-byte
+//    row-contiguous global stores (the coalesced linear output traversal of
+//    the XLA:GPU emitters page, loop emitter, with wider vectors).
+//  * Workgroup -> tile mapping gives each of the 8 XCDs a contiguous range of
+//    tiles and rasterises tiles in groups of `group_m` tile rows, so the
+//    workgroups that share an XCD's L2 share A and B panels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace spg {
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef short shortx8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#define SPG_LDS __attribute__((address_space(3)))
+
+constexpr int kBK = 64;                  // K extent of one stage: 64 halves = 128 B per row
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past any num_records: loads 0
+
+enum { kOutF16 = 0, kOutBF16 = 1, kOutF32 = 2 };
+enum { kEpiNone = 0, kEpiGelu = 1 };
+
+struct KArgs {
+    const uint16_t* A;
+    const uint16_t* B;
+    void* C;
+    int32_t M, N, K;
+    int32_t tiles_m, tiles_n;
+    int32_t group_m;
+    int32_t xcd_remap;
+    int32_t out_dtype;
+    int32_t epilogue;
+};
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    // word 3 = 0x00020000: 32-bit data format, raw (stride 0) buffer on gfx9
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_dst, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SPG_LDS void*)lds_dst, 16, (int)voff, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory instructions of this wave are outstanding.
+// gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14];
+// expcnt and lgkmcnt are left at their maxima (no wait on them).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt out of range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Swizzle of K-contiguous tiles (A, and B stored [N,K]): a row holds 64 halves
+// = 8 chunks of 16 B; logical chunk c of row r lives at chunk c ^ kswz(r).
+// Rows r..r+7 get distinct XOR values and rows r, r+8 differ in the low bit,
+// so 8 consecutive lanes (one 128-B bank sweep) or 16 (one 256-B sweep) reading
+// the same logical chunk of consecutive rows never share a bank.
+__device__ __forceinline__ int kswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Swizzle of N-contiguous B tiles ([K,N] storage): the 16-B chunk index of row
+// k is XOR-ed with {0, 6, 12, 10}[k & 3].  A transposing read covers 4
+// consecutive rows; this table gives those 4 rows distinct 32-B windows within
+// 128 B and distinct 64-B windows within 256 B.
+__device__ __forceinline__ int nswz(int k) { return (0xAC60 >> ((k & 3) * 4)) & 15; }
+
+__device__ __forceinline__ float gelu_tanh(float x) {
+    // 0.5 x (1 + tanh(u)) == x * sigmoid(2u) == x / (1 + exp(-2u)),
+    // u = 0.7978845608 (x + 0.044715 x^3).  exp via v_exp_f32 (2^x); the
+    // form saturates cleanly: exp -> inf gives -0, exp -> 0 gives x.
+    float u = 0.7978845608f * (x + 0.044715f * x * x * x);
+    float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * u);  // 2*log2(e) = 2.885...
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ float epi_apply(float x, int epi) {
+    return epi == kEpiGelu ? gelu_tanh(x) : x;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bits(float x, bool bf16) {
+    if (bf16) return __builtin_bit_cast(uint16_t, (__bf16)x);   // v_cvt_pk_bf16_f32, RNE
+    return __builtin_bit_cast(uint16_t, (_Float16)x);            // v_cvt_f16_f32, RNE
+}
+
+__device__ __forceinline__ float bits_to_f32(uint16_t b, bool bf16) {
+    if (bf16) return __builtin_bit_cast(float, (uint32_t)b << 16);
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Workgroup id -> (tile row, tile column).
+__device__ __forceinline__ void tile_of(int wg, const KArgs& a, int& tm, int& tn) {
+    const int T = a.tiles_m * a.tiles_n;
+    if (a.xcd_remap) {
+        // workgroups are dispatched round-robin over the 8 XCDs (wg % 8); hand XCD x
+        // the contiguous tile range [x*q + min(x, r), ...) of its share
+        const int x = wg & 7, i = wg >> 3, q = T >> 3, r = T & 7;
+        wg = x * q + (x < r ? x : r) + i;
+    }
+    const int gsz = a.group_m * a.tiles_n;
+    const int g = wg / gsz;
+    const int first = g * a.group_m;
+    const int rem = a.tiles_m - first;
+    const int gm = rem < a.group_m ? rem : a.group_m;
+    const int in = wg - g * gsz;
+    tm = first + in % gm;
+    tn = in / gm;
+}
+
+template <bool BF16>
+__device__ __forceinline__ floatx16 mfma(const u32x4& x, const u32x4& y, const floatx16& c) {
+    if constexpr (BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x),
+                                                       __builtin_bit_cast(bf16x8, y), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, x),
+                                                      __builtin_bit_cast(halfx8, y), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// the pipelined kernel
+// ---------------------------------------------------------------------------
+
+// Epilogue of one wave: accumulator -> (GELU) -> output type -> LDS staging ->
+// 16-byte row-contiguous global stores.  The wave's C tile is processed 32 rows
+// (one MFMA block row) at a time through a private 32 x WN staging buffer whose
+// 16-B chunks are XOR-swizzled by row so that both the 4-value writes (32 rows,
+// same column) and the row reads are free of bank conflicts.
+template <int OD, bool GELU, int TM, int TN, int WN>
+__device__ __forceinline__ void store_tile(const floatx16 (&acc)[TN][TM], char* stg,
+                                           const KArgs& args, int m_base, int n_base, int lane) {
+    constexpr int OB = OD == kOutF32 ? 4 : 2;         // output bytes
+    constexpr int ROWB = WN * OB;                     // staged row bytes
+    constexpr int CPR = ROWB / 16;                    // 16-B chunks per staged row
+    constexpr int E16 = 16 / OB;                      // outputs per chunk
+    static_assert(CPR == 8 || CPR == 16 || CPR == 32, "staging swizzle assumes 8..32 chunks");
+    auto swz = [](int row) { return CPR >= 16 ? (row & 15) : ((row >> 1) & 7); };
+    const int M = args.M, N = args.N;
+    const bool vec_ok = (N % E16) == 0;
+    const int lrow = lane & 31;
+#pragma unroll
+    for (int bm = 0; bm < TM; ++bm) {
+        // 1) lane holds C[row l%32][cols bn*32 + 8q + 4(l/32) + 0..3]
+#pragma unroll
+        for (int bn = 0; bn < TN; ++bn) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = acc[bn][bm][4 * q + e];
+                    if constexpr (GELU) v[e] = gelu_tanh(v[e]);
+                }
+                const int byte = (bn * 32 + 8 * q + 4 * (lane >> 5)) * OB;
+                char* dst = stg + lrow * ROWB + (((byte >> 4) ^ swz(lrow)) << 4) + (byte & 15);
+                if constexpr (OD == kOutF32) {
+                    *(SPG_LDS u32x4*)dst = u32x4{__builtin_bit_cast(uint32_t, v[0]),
+                                                 __builtin_bit_cast(uint32_t, v[1]),
+                                                 __builtin_bit_cast(uint32_t, v[2]),
+                                                 __builtin_bit_cast(uint32_t, v[3])};
+                } else {
+                    constexpr bool BF = OD == kOutBF16;
+                    const uint32_t p0 = (uint32_t)f32_to_bits(v[0], BF) | ((uint32_t)f32_to_bits(v[1], BF) << 16);
+                    const uint32_t p1 = (uint32_t)f32_to_bits(v[2], BF) | ((uint32_t)f32_to_bits(v[3], BF) << 16);
+                    *(SPG_LDS u32x2*)dst = u32x2{p0, p1};
+                }
+            }
+        }
+        // 2) LDS -> global, 16 B per lane, consecutive lanes along a row
+#pragma unroll 1
+        for (int it = 0; it < (32 * CPR) / 64; ++it) {
+            const int idx = it * 64 + lane;
+            const int row = idx / CPR;
+            const int ch = idx % CPR;
+            const u32x4 val = *(const SPG_LDS u32x4*)(stg + row * ROWB + ((ch ^ swz(row)) << 4));
+            const int gm = m_base + bm * 32 + row;
+            const int gn = n_base + ch * E16;
+            if (gm < M && gn < N) {
+                char* dstg = (char*)args.C + ((size_t)gm * N + gn) * OB;
+                if (vec_ok && gn + E16 <= N) {
+                    *(u32x4*)dstg = val;
+                } else {
+                    const int lim = (N - gn) < E16 ? (N - gn) : E16;
+                    for (int e = 0; e < lim; ++e) {
+                        if constexpr (OB == 4) ((uint32_t*)dstg)[e] = val[e];
+                        else ((uint16_t*)dstg)[e] = (uint16_t)(val[e >> 1] >> ((e & 1) * 16));
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int S>
+struct Geom {
+    static constexpr int WAVES_N = BN / WN;
+    static constexpr int NW = (BM / WM) * WAVES_N;
+    static constexpr int NT = NW * 64;
+    static constexpr int TM = WM / 32, TN = WN / 32;
+    static constexpr int A_BYTES = BM * kBK * 2;
+    static constexpr int B_BYTES = BN * kBK * 2;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int A_DMA = A_BYTES / 1024 / NW;  // DMA instructions per wave per k-tile
+    static constexpr int B_DMA = B_BYTES / 1024 / NW;
+    static constexpr int L = A_DMA + B_DMA;
+    static constexpr int STG = 32 * WN * 4;            // epilogue staging bytes per wave (fp32 worst case)
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile shape");
+    static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "DMA split");
+    static_assert(S >= 1 && S <= 4, "stages");
+    static_assert(S * STAGE <= 160 * 1024, "LDS budget");
+    static_assert(((NW + S - 1) / S) * STG <= STAGE, "epilogue staging must fit the ring");
+    static_assert((S > 2 ? (S - 2) * L : 0) < 64, "vmcnt range");
+};
+
+template <bool BF16, bool B_NK, int BM, int BN, int WM, int WN, int S, bool SWZ>
+__global__ void __launch_bounds__((Geom<BM, BN, WM, WN, S>::NT))
+pipelined_gemm(KArgs args) {
+    using G = Geom<BM, BN, WM, WN, S>;
+    constexpr int TM = G::TM, TN = G::TN, A_BYTES = G::A_BYTES;
+    constexpr int A_DMA = G::A_DMA, B_DMA = G::B_DMA;
+
+    __shared__ __attribute__((aligned(1024))) char ring0[G::STAGE];
+    __shared__ __attribute__((aligned(1024))) char ring1[S > 1 ? G::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char ring2[S > 2 ? G::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char ring3[S > 3 ? G::STAGE : 16];
+
+    // ring slot s as a compile-time choice of array (see the header comment)
+    auto slot_of = [&](auto sc) -> char* {
+        if constexpr (decltype(sc)::value == 0) return ring0;
+        else if constexpr (decltype(sc)::value == 1) return ring1;
+        else if constexpr (decltype(sc)::value == 2) return ring2;
+        else return ring3;
+    };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / G::WAVES_N;
+    const int wn = wave % G::WAVES_N;
+
+    int tm, tn;
+    tile_of(blockIdx.x, args, tm, tn);
+    const int M = args.M, N = args.N, K = args.K;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nk = (K + kBK - 1) / kBK;
+
+    // ---- buffer resources: bytes past the end read as zero -------------------
+    const int a_rows = (M - m0) < BM ? (M - m0) : BM;
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc(args.A + (size_t)m0 * K, (uint32_t)a_rows * (uint32_t)K * 2u);
+    __amdgpu_buffer_rsrc_t rB;
+    if constexpr (B_NK) {
+        const int b_rows = (N - n0) < BN ? (N - n0) : BN;
+        rB = make_rsrc(args.B + (size_t)n0 * K, (uint32_t)b_rows * (uint32_t)K * 2u);
+    } else {
+        // rows k >= K fall past num_records; columns past N are masked per lane
+        rB = make_rsrc(args.B + n0, (uint32_t)(((size_t)K * N - n0) * 2u));
+    }
+
+    // ---- per-lane DMA source offsets (k-tile 0) ------------------------------
+    uint32_t offA[A_DMA];
+    int colA[A_DMA];
+#pragma unroll
+    for (int j = 0; j < A_DMA; ++j) {
+        const int d = wave * A_DMA + j;
+        const int r = d * 8 + (lane >> 3);
+        const int p = lane & 7;
+        const int c = SWZ ? (p ^ kswz(r)) : p;
+        offA[j] = (uint32_t)r * (uint32_t)K * 2u + (uint32_t)c * 16u;
+        colA[j] = c * 8;
+    }
+    uint32_t offB[B_DMA];
+    int colB[B_DMA];
+#pragma unroll
+    for (int j = 0; j < B_DMA; ++j) {
+        const int d = wave * B_DMA + j;
+        if constexpr (B_NK) {
+            const int r = d * 8 + (lane >> 3);
+            const int p = lane & 7;
+            const int c = SWZ ? (p ^ kswz(r)) : p;
+            offB[j] = (uint32_t)r * (uint32_t)K * 2u + (uint32_t)c * 16u;
+            colB[j] = c * 8;
+        } else {
+            constexpr int CPR = BN / 8;          // 16-B chunks per row
+            constexpr int RP = 64 / CPR;         // rows per wave instruction
+            const int r = d * RP + lane / CPR;
+            const int p = lane % CPR;
+            const int c = SWZ ? (p ^ nswz(r)) : p;
+            offB[j] = (uint32_t)r * (uint32_t)N * 2u + (uint32_t)c * 16u;
+            colB[j] = c * 8;
+        }
+    }
+    const bool k_tail = (K % kBK) != 0;
+    const bool n_tail = !B_NK && (n0 + BN > N);
+
+    auto issue = [&](char* slot, int kt) __attribute__((always_inline)) {
+        const int k0 = kt * kBK;
+        const bool last = k_tail && (kt == nk - 1);
+#pragma unroll
+        for (int j = 0; j < A_DMA; ++j) {
+            uint32_t off = offA[j] + (uint32_t)k0 * 2u;
+            if (last && k0 + colA[j] + 8 > K) off = kOOB;
+            dma16(rA, slot + (wave * A_DMA + j) * 1024, off);
+        }
+#pragma unroll
+        for (int j = 0; j < B_DMA; ++j) {
+            uint32_t off;
+            if constexpr (B_NK) {
+                off = offB[j] + (uint32_t)k0 * 2u;
+                if (last && k0 + colB[j] + 8 > K) off = kOOB;
+            } else {
+                off = offB[j] + (uint32_t)k0 * (uint32_t)N * 2u;
+                if (n_tail && n0 + colB[j] + 8 > N) off = kOOB;
+            }
+            dma16(rB, slot + A_BYTES + (wave * B_DMA + j) * 1024, off);
+        }
+    };
+
+    // ---- per-lane LDS read offsets -------------------------------------------
+    // A (second MFMA operand): lane l reads row wm*WM + bm*32 + l%32,
+    // k = kk*16 + (l/32)*8 .. +7  (16-B chunk 2kk + l/32).
+    int aoff[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const int c = kk * 2 + (lane >> 5);
+        const int r = lane & 31;
+        aoff[kk] = (wm * WM + r) * 128 + (SWZ ? (c ^ kswz(r)) : c) * 16;
+    }
+    // B (first MFMA operand): lane l needs column n = wn*WN + bn*32 + l%32 with the
+    // same 8 k values as A.
+    int boff[B_NK ? 4 : TN];
+    if constexpr (B_NK) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int c = kk * 2 + (lane >> 5);
+            const int r = lane & 31;
+            boff[kk] = A_BYTES + (wn * WN + r) * 128 + (SWZ ? (c ^ kswz(r)) : c) * 16;
+        }
+    } else {
+        // ds_read_b64_tr_b16: in each 16-lane group, lane i supplies 8 B of row
+        // (k0 + i/4) at columns (n0 + 4*(i%4)) .. +3 and receives column n0 + i of
+        // rows k0..k0+3.  Lanes 16-31 take columns +16, lanes 32-63 rows +8.
+        constexpr int RB = BN * 2;
+        const int kl = (lane >> 5) * 8 + ((lane & 15) >> 2);
+#pragma unroll
+        for (int bn = 0; bn < TN; ++bn) {
+            const int chunk = (wn * WN + bn * 32) / 8 + ((lane >> 4) & 1) * 2 + ((lane >> 1) & 1);
+            boff[bn] = A_BYTES + kl * RB + (SWZ ? (chunk ^ nswz(kl)) : chunk) * 16 + (lane & 1) * 8;
+        }
+    }
+
+    floatx16 acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // Operand fragments of one 16-wide k step: A rows (second MFMA operand) and
+    // B columns (first MFMA operand).  Two sets alternate so that the LDS reads of
+    // step kk+1 are in flight while the MFMAs of step kk run.
+    struct Frags {
+        u32x4 a[TM];
+        u32x4 b[TN];
+    };
+    auto load_frags = [&](const char* slot, int kk, Frags& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int bm = 0; bm < TM; ++bm)
+            f.a[bm] = *(const SPG_LDS u32x4*)(slot + aoff[kk] + bm * 32 * 128);
+#pragma unroll
+        for (int bn = 0; bn < TN; ++bn) {
+            if constexpr (B_NK) {
+                f.b[bn] = *(const SPG_LDS u32x4*)(slot + boff[kk] + bn * 32 * 128);
+            } else {
+                constexpr int RB = BN * 2;
+                const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (SPG_LDS shortx4*)(slot + boff[bn] + (kk * 16) * RB));
+                const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (SPG_LDS shortx4*)(slot + boff[bn] + (kk * 16 + 4) * RB));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+                const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+                f.b[bn] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+            }
+        }
+    };
+    auto mma = [&](const Frags& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int bn = 0; bn < TN; ++bn)
+#pragma unroll
+            for (int bm = 0; bm < TM; ++bm)
+                acc[bn][bm] = mfma<BF16>(f.b[bn], f.a[bm], acc[bn][bm]);
+    };
+    // keep each stage's loads and MFMAs together: no motion across stage boundaries
+    auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+
+    // ---- the pipelined K loop ----------------------------------------------------
+    //
+    // One k-tile = 4 MFMA stages (kk = 0..3, 16 k each).  Stage kk issues the LDS
+    // reads of stage kk+1 and then the MFMAs of stage kk.  Between stages 2 and 3 --
+    // after this wave's last LDS read of the current slot -- sits the one barrier of
+    // the k-tile: once every wave has passed it, (a) the next k-tile, whose DMA this
+    // wave has waited for, is visible to all, and (b) nobody reads the current slot
+    // any more, so it is released and refilled with k-tile t+S while the MFMAs of
+    // stage 3 (which read registers, not LDS) still run.  Stage 3 also issues the
+    // first LDS reads of the next k-tile, so the matrix pipe has work across the
+    // k-tile boundary.
+    Frags f0, f1;
+    if constexpr (S == 1) {
+        // the serial K loop: copy, wait, multiply, and only then let the next copy in
+        for (int t = 0; t < nk; ++t) {
+            issue(ring0, t);
+            wait_vmcnt<0>();
+            __syncthreads();
+            load_frags(ring0, 0, f0);
+            load_frags(ring0, 1, f1);
+            fence();
+            mma(f0);
+            load_frags(ring0, 2, f0);
+            fence();
+            mma(f1);
+            load_frags(ring0, 3, f1);
+            fence();
+            mma(f0);
+            fence();
+            mma(f1);
+            __syncthreads();
+        }
+    } else {
+        // prologue: k-tiles 0 .. S-1 fill every slot
+        static_for<0, S>([&](auto sc) {
+            if (sc.value < nk) issue(slot_of(sc), sc.value);
+        });
+        if (nk >= S) wait_vmcnt<(S - 1) * G::L>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        load_frags(ring0, 0, f0);
+
+        constexpr int STEADY = (S - 2) * G::L;
+        // k-tile t (< nk) in slot s.  FULL (compile-time) means t+S < nk: the k-tiles
+        // t+1 .. t+S-1 are all in flight, exactly the copies of t+2 .. t+S-1 may stay
+        // outstanding, and slot s is refilled with k-tile t+S.  Otherwise the same
+        // decisions are taken at run time; only the boundary (wait, barrier, refill,
+        // next reads) is conditional, never the MFMAs.
+        auto ktile = [&](auto sc, int t, auto full) __attribute__((always_inline)) {
+            constexpr int s = decltype(sc)::value;
+            constexpr bool FULL = decltype(full)::value;
+            const char* cur = slot_of(sc);
+            const char* nxt = slot_of(std::integral_constant<int, (s + 1) % S>{});
+            load_frags(cur, 1, f1);
+            fence();
+            mma(f0);
+            load_frags(cur, 2, f0);
+            fence();
+            mma(f1);
+            load_frags(cur, 3, f1);
+            fence();
+            mma(f0);
+            fence();
+            if (FULL || t + 1 < nk) {
+                if (FULL || t + S < nk) wait_vmcnt<STEADY>();
+                else wait_vmcnt<0>();
+                __syncthreads();
+                if (FULL || t + S < nk) issue(slot_of(sc), t + S);
+                load_frags(nxt, 0, f0);
+            }
+            fence();
+            mma(f1);
+        };
+        // steady state: S k-tiles per iteration, static slots, no branches
+        int t0 = 0;
+        for (; t0 + 2 * S <= nk; t0 += S) {
+            static_for<0, S>([&](auto sc) {
+                ktile(sc, t0 + decltype(sc)::value, std::true_type{});
+            });
+        }
+        // drain: fewer than 2S k-tiles remain; t0 is a multiple of S
+        static_for<0, 2 * S - 1>([&](auto sc) {
+            constexpr int i = decltype(sc)::value;
+            const int t = t0 + i;
+            if (t < nk) ktile(std::integral_constant<int, i % S>{}, t, std::false_type{});
+        });
+    }
+
+    // ---- epilogue ------------------------------------------------------------
+    __syncthreads();  // the ring is drained and free for staging
+    char* stg;
+    {
+        const int sl = wave % S;
+        char* base = sl == 0 ? ring0 : sl == 1 ? ring1 : sl == 2 ? ring2 : ring3;
+        stg = base + (wave / S) * G::STG;
+    }
+    // one branch on the (uniform) output type and epilogue, outside all accumulator reads
+    const int od = args.out_dtype;
+    const bool ge = args.epilogue == kEpiGelu;
+    const int m_base = m0 + wm * WM, n_base = n0 + wn * WN;
+    if (od == kOutF32) {
+        if (ge) store_tile<kOutF32, true, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+        else store_tile<kOutF32, false, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+    } else if (od == kOutBF16) {
+        if (ge) store_tile<kOutBF16, true, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+        else store_tile<kOutBF16, false, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+    } else {
+        if (ge) store_tile<kOutF16, true, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+        else store_tile<kOutF16, false, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// simple kernel: any shape, any alignment, any K (including 0)
+// ---------------------------------------------------------------------------
+
+template <bool BF16, bool B_NK>
+__global__ void __launch_bounds__(256) simple_gemm(KArgs a) {
+    constexpr int T = 64, TK = 16;
+    __shared__ float As[TK][T + 1];
+    __shared__ float Bs[TK][T + 1];
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+    const int m0 = blockIdx.y * T, n0 = blockIdx.x * T;
+    const int M = a.M, N = a.N, K = a.K;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < K; k0 += TK) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + i * 256;
+            const int r = e / TK, kk = e % TK;
+            const int gm = m0 + r, gk = k0 + kk;
+            As[kk][r] = (gm < M && gk < K) ? bits_to_f32(a.A[(size_t)gm * K + gk], BF16) : 0.0f;
+            const int kb = e / T, c = e % T;
+            const int gkb = k0 + kb, gn = n0 + c;
+            float bv = 0.0f;
+            if (gkb < K && gn < N)
+                bv = bits_to_f32(B_NK ? a.B[(size_t)gn * K + gkb] : a.B[(size_t)gkb * N + gn], BF16);
+            Bs[kb][c] = bv;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < TK; ++kk) {
+            float av[4], bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int gm = m0 + ty * 4 + i;
+        if (gm >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int gn = n0 + tx * 4 + j;
+            if (gn >= N) continue;
+            const float v = epi_apply(acc[i][j], a.epilogue);
+            const size_t o = (size_t)gm * N + gn;
+            if (a.out_dtype == kOutF32) ((float*)a.C)[o] = v;
+            else ((uint16_t*)a.C)[o] = f32_to_bits(v, a.out_dtype == kOutBF16);
+        }
+    }
+}
+
+}  // namespace spg

@@ -1,0 +1,140 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every declared
+symbol, validates arguments before any HIP call, and its host-side planning logic
+(configuration table, LDS budget, heuristic) behaves as documented.  No kernel runs."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import software_pipelined_tiled_gemm_amd as spg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spgemm.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(spg.LIB_PATH):
+        pytest.fail("libspgemm.so is not built; run __graft_entry__.build()")
+    return spg.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert set(names) == set(spg.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code, text in spg.STATUS.items():
+        assert spg.gemm_status_string(code) == text
+
+
+def test_invalid_arguments_rejected_without_gpu(L):
+    h = ctypes.c_void_p()
+    ok = lambda *a: L.gemm_create(ctypes.byref(h), *a, None)
+    assert L.gemm_create(None, 8, 8, 8, 0, 0, 0, 0, None) == 1
+    assert ok(-1, 8, 8, 0, 0, 0, 0) == 1
+    assert ok(8, -1, 8, 0, 0, 0, 0) == 1
+    assert ok(8, 8, -1, 0, 0, 0, 0) == 1
+    assert ok(8, 8, 8, 2, 0, 0, 0) == 1    # fp32 input is not supported
+    assert ok(8, 8, 8, 7, 0, 0, 0) == 1    # unknown input dtype
+    assert ok(8, 8, 8, 0, 9, 0, 0) == 1    # unknown output dtype
+    assert ok(8, 8, 8, 0, 0, 2, 0) == 1    # unknown layout
+    assert ok(8, 8, 8, 0, 0, 0, 5) == 1    # unknown epilogue
+    assert ok(1 << 40, 8, 8, 0, 0, 0, 0) == 2
+    # NULL handle / pointers
+    assert L.gemm_run(None, None, None, None, None) == 1
+    assert L.gemm_get_config(None, None) == 1
+    assert L.gemm_autotune(None, None, None, None, None, 1, None) == 1
+    assert L.gemm_destroy(None) == 0
+
+
+def test_plan_lifecycle_and_pointer_checks(L):
+    h = spg.gemm_create(64, 64, 64, "f16", "f16", "nk")
+    try:
+        cfg = spg.gemm_get_config(h)
+        assert cfg.block_k == 64 and cfg.stages >= 2
+        # non-empty problem with NULL operands: rejected before any launch
+        assert L.gemm_run(h, None, None, None, None) == 1
+        assert L.gemm_run(h, None, None, 4096, None) == 1
+    finally:
+        spg.gemm_destroy(h)
+    # an empty problem is a successful no-op even with NULL pointers
+    h = spg.gemm_create(0, 64, 64, "f16", "f16", "nk")
+    assert L.gemm_run(h, None, None, None, None) == 0
+    spg.gemm_destroy(h)
+
+
+def test_forced_configs(L):
+    n = spg.gemm_num_configs()
+    assert n >= 8
+    for i in range(n):
+        c = spg.gemm_list_config(i)
+        assert spg.gemm_lds_bytes(c) <= 160 * 1024
+        h = spg.gemm_create(1000, 1000, 1000, "bf16", "bf16", "kn", "none", c)
+        got = spg.gemm_get_config(h)
+        assert got.as_dict()["block_m"] == c.block_m and got.stages == c.stages
+        spg.gemm_destroy(h)
+    bad = spg.TileConfig(block_m=256, block_n=256, block_k=64, stages=3, wave_m=128,
+                         wave_n=128, swizzle=1, group_m=4, xcd_remap=1)
+    with pytest.raises(spg.GemmError) as e:   # 192 KiB of LDS: over the 160 KiB budget
+        spg.gemm_create(512, 512, 512, force=bad)
+    assert e.value.status == 2
+    odd = spg.TileConfig(block_m=96, block_n=128, block_k=64, stages=2, wave_m=32, wave_n=64,
+                         swizzle=1, group_m=4, xcd_remap=1)
+    with pytest.raises(spg.GemmError) as e:
+        spg.gemm_create(512, 512, 512, force=odd)
+    assert e.value.status == 2
+    neg = spg.TileConfig(block_m=128, block_n=128, block_k=64, stages=2, wave_m=64, wave_n=64,
+                         swizzle=3, group_m=4, xcd_remap=1)
+    with pytest.raises(spg.GemmError) as e:
+        spg.gemm_create(512, 512, 512, force=neg)
+    assert e.value.status == 1
+
+
+def test_lds_budget_is_the_tilelang_formula(L):
+    # stages * (block_M*block_K + block_N*block_K) * elem_bytes, evaluated at the
+    # TileLang tutorial's defaults (golden file)
+    for line in open(os.path.join(GOLDEN, "tilelang_smem_budget.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        bm, bn, bk, eb, st, want = map(int, line.split())
+        assert eb == 2
+        c = spg.TileConfig(block_m=bm, block_n=bn, block_k=bk, stages=st, wave_m=32, wave_n=32)
+        assert spg.gemm_lds_bytes(c) == want
+
+
+def test_unaligned_shapes_plan_the_simple_kernel(L):
+    # K % 8 != 0 cannot feed 16-byte direct-to-LDS copies: the plan reports block_k = 0
+    h = spg.gemm_create(100, 100, 77, "f16", "f16", "nk")
+    assert spg.gemm_get_config(h).block_k == 0
+    spg.gemm_destroy(h)
+    h = spg.gemm_create(100, 101, 64, "bf16", "bf16", "kn")   # [K,N] rows not 16-B
+    assert spg.gemm_get_config(h).block_k == 0
+    spg.gemm_destroy(h)
+    h = spg.gemm_create(100, 101, 64, "bf16", "bf16", "nk")   # [N,K] rows are 16-B
+    assert spg.gemm_get_config(h).block_k == 64
+    spg.gemm_destroy(h)
+
+
+def test_heuristic_tiles(L):
+    def cfg(M, N, K):
+        h = spg.gemm_create(M, N, K, "bf16", "bf16", "kn")
+        c = spg.gemm_get_config(h)
+        spg.gemm_destroy(h)
+        return c
+    big = cfg(8192, 8192, 8192)
+    assert (big.block_m, big.block_n) in ((256, 256), (256, 128), (128, 256))
+    small = cfg(256, 256, 256)
+    assert (small.block_m, small.block_n) == (128, 128)

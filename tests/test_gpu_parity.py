@@ -1,0 +1,181 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Tolerance (the accepted reading of the bound): with s = sqrt(K) max|A| max|B|,
+fp32 output: max|C - C_ref| / s <= 1e-4; fp16/bf16 output: the error in excess
+of half an output ulp of C_ref, divided by s, <= 4e-3 (the literal err_lit is
+reported too).  Small and medium shapes compare every element; the full-size
+workloads compare whole sampled rows (all N columns of each) because the fp64
+oracle cannot do 10^12 flops in a test, plus properties of the whole C.
+"""
+
+import numpy as np
+import pytest
+
+import software_pipelined_tiled_gemm_amd as spg
+import workloads as W
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _variants():
+    return [spg.gemm_list_config(i) for i in range(spg.gemm_num_configs())]
+
+
+# ---------------------------------------------------------------------------
+# every compiled configuration, both layouts, both input dtypes, ragged shape
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("in_dtype", [W.F16, W.BF16])
+@pytest.mark.parametrize("b_layout", [W.B_KN, W.B_NK])
+def test_all_variants_ragged(in_dtype, b_layout):
+    # spans several 256-tiles in M and N with ragged edges, and a K tail (K % 64 = 40)
+    w = W.custom(520, 648, 616, in_dtype, in_dtype, b_layout, "none", ("uniform", -1.0, 1.0))
+    a, b = W.make_inputs(w)
+    results = {}
+    for cfg in _variants():
+        _log(f"variant {cfg} {w.describe()}")
+        C, used = G.run(w, a, b, force=cfg)
+        got = G.c_values(C, w)
+        G.check(w, a, b, got)
+        results[repr(cfg)] = got
+    # every pipelined configuration keeps the same per-element k order (k-tiles in
+    # ascending order, 16-wide MFMA steps in ascending order), so the results must
+    # be bitwise identical: a slot reused too early would break this
+    vals = list(results.values())
+    for v in vals[1:]:
+        assert np.array_equal(v, vals[0])
+
+
+@pytest.mark.parametrize("out_dtype", [W.F16, W.BF16, W.F32])
+@pytest.mark.parametrize("epilogue", ["none", "gelu_tanh"])
+def test_output_dtypes_and_epilogue(out_dtype, epilogue):
+    for b_layout in (W.B_KN, W.B_NK):
+        w = W.custom(384, 392, 320, W.BF16, out_dtype, b_layout, epilogue, ("normal", 0.3))
+        a, b = W.make_inputs(w)
+        _log(w.describe())
+        C, _ = G.run(w, a, b)
+        G.check(w, a, b, G.c_values(C, w))
+
+
+# ---------------------------------------------------------------------------
+# small shapes: masks on M, N and K, and the simple kernel for unaligned K / N
+# ---------------------------------------------------------------------------
+
+SIZES = [1, 2, 3, 7, 8, 15, 16, 17, 31, 33, 63, 64, 65, 127, 129]
+
+
+def _small_cases():
+    r = np.random.Generator(np.random.PCG64(2024))
+    cases = set()
+    for M in SIZES:
+        cases.add((M, int(r.choice(SIZES)), int(r.choice(SIZES))))
+    for N in SIZES:
+        cases.add((int(r.choice(SIZES)), N, int(r.choice(SIZES))))
+    for K in SIZES:
+        cases.add((int(r.choice(SIZES)), int(r.choice(SIZES)), K))
+    cases.update({(1, 1, 1), (129, 129, 129), (64, 64, 64), (8, 8, 8), (65, 65, 72)})
+    return sorted(cases)
+
+
+@pytest.mark.parametrize("b_layout", [W.B_KN, W.B_NK])
+@pytest.mark.parametrize("in_dtype", [W.F16, W.BF16])
+def test_small_shapes(b_layout, in_dtype):
+    for (M, N, K) in _small_cases():
+        for out_dtype, epi in ((in_dtype, "none"), (W.F32, "gelu_tanh")):
+            w = W.custom(M, N, K, in_dtype, out_dtype, b_layout, epi)
+            a, b = W.make_inputs(w)
+            C, cfg = G.run(w, a, b)
+            G.check(w, a, b, G.c_values(C, w))
+
+
+def test_empty_and_k_zero():
+    import torch
+    # M == 0 / N == 0: no-op
+    for (M, N) in ((0, 16), (16, 0)):
+        w = W.custom(M, N, 32, W.F16, W.F16, W.B_NK)
+        a, b = W.make_inputs(w)
+        G.run(w, a, b)
+    # K == 0: C = epi(0) = 0 everywhere, written over a non-zero fill
+    for epi in ("none", "gelu_tanh"):
+        w = W.custom(40, 24, 0, W.BF16, W.F32, W.B_KN, epi)
+        a, b = W.make_inputs(w)
+        C = G.alloc_c(w, fill=7)
+        G.run(w, a, b, C=C)
+        assert torch.all(C == 0)
+
+
+def test_misaligned_pointers_take_the_simple_path():
+    import torch
+    w = W.custom(100, 72, 64, W.F16, W.F16, W.B_NK)
+    a, b = W.make_inputs(w)
+    A = torch.zeros(a.size + 1, dtype=torch.int16, device=G.torch_dev())
+    A[1:] = G.to_dev(a).reshape(-1)
+    B = G.to_dev(b)
+    C = G.alloc_c(w)
+    with spg.Gemm(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.b_layout) as g:
+        g(A[1:].data_ptr(), B, C)     # A is only 2-byte aligned
+    torch.cuda.synchronize()
+    G.check(w, a, b, G.c_values(C, w))
+
+
+def test_deterministic_and_untouched_outside():
+    import torch
+    w = W.custom(300, 200, 256, W.BF16, W.BF16, W.B_KN)
+    a, b = W.make_inputs(w)
+    A, B = G.to_dev(a), G.to_dev(b)
+    big = torch.full((w.M + 2, w.N), 0x5A5A, dtype=torch.int16, device=G.torch_dev())
+    C = big[1:-1]
+    with spg.Gemm(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.b_layout) as g:
+        g(A, B, C)
+        first = C.clone()
+        g(A, B, C)
+    torch.cuda.synchronize()
+    assert torch.equal(first, C)
+    assert torch.all(big[0] == 0x5A5A) and torch.all(big[-1] == 0x5A5A)
+
+
+def test_autotune_keeps_parity():
+    w = W.custom(1024, 768, 512, W.F16, W.F16, W.B_NK)
+    a, b = W.make_inputs(w)
+    C, cfg = G.run(w, a, b, autotune=True)
+    _log(f"autotuned {cfg}")
+    assert cfg.block_k == 64 and cfg.stages >= 2
+    G.check(w, a, b, G.c_values(C, w))
+
+
+# ---------------------------------------------------------------------------
+# the benchmark workloads at full size, in the configuration the benchmark times
+# ---------------------------------------------------------------------------
+
+FULL = ["tn_f16_256", "tn_f16_3000x5000x1000_f32out", "pallas_hopper_example",
+        "tn_f16_4096", "nn_bf16_3072x4096x4096_gelu", "nn_bf16_8192", "nn_f16_8192"]
+SAMPLE_ROWS = {"tn_f16_4096": 96, "nn_bf16_3072x4096x4096_gelu": 96, "nn_bf16_8192": 48,
+               "nn_f16_8192": 48}
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload_full_size(name):
+    import torch
+    w = W.WORKLOADS[name]
+    _log(f"workload {name}: {w.describe()}")
+    a, b = W.make_inputs(w)
+    C, cfg = G.run(w, a, b)
+    _log(f"  config {cfg}")
+    n = SAMPLE_ROWS.get(name)
+    if n is None:
+        G.check(w, a, b, G.c_values(C, w))
+        return
+    r = np.random.Generator(np.random.PCG64(77))
+    rows = np.sort(np.concatenate([[0, w.M - 1], r.choice(w.M, n - 2, replace=False)]))
+    res = G.check(w, a, b, G.c_values(C, w, rows), rows=rows)
+    _log(f"  sampled rows: err_lit={res['err_lit']:.3e} floor={res['floor']:.3e} "
+         f"err_q={res['err_q']:.3e}")
+    # whole-C property: finite everywhere
+    Cf = C.float() if w.out_dtype == W.F32 else (
+        C.view(torch.bfloat16).float() if w.out_dtype == W.BF16 else C.view(torch.float16).float())
+    assert bool(torch.isfinite(Cf).all())
