@@ -74,20 +74,43 @@ def cpu_baseline(w, target_s=15.0):
 
     a, b = W.make_inputs(w)
     o = oracle.default()
-    # calibrate on 4 rows, then size the sample to ~target_s
-    t0 = time.perf_counter()
-    o.gemm(a, b, w.M, w.N, w.K, w.in_dtype, w.b_layout, w.epilogue, rows=list(range(8)))
-    dt = time.perf_counter() - t0
-    rows = int(max(8, min(w.M, 8 * target_s / max(dt, 1e-3))))
-    rows = max(o.num_threads(), rows - rows % max(1, o.num_threads()))
-    sel = np.linspace(0, w.M - 1, rows).astype(np.int64)
-    t0 = time.perf_counter()
-    o.gemm(a, b, w.M, w.N, w.K, w.in_dtype, w.b_layout, w.epilogue, rows=sel)
-    dt = time.perf_counter() - t0
+    nt = max(1, o.num_threads())
+
+    def run(nrows):
+        sel = np.linspace(0, w.M - 1, nrows).astype(np.int64)
+        t0 = time.perf_counter()
+        o.gemm(a, b, w.M, w.N, w.K, w.in_dtype, w.b_layout, w.epilogue, rows=sel)
+        return time.perf_counter() - t0
+
+    # two-point calibration separates the fixed cost (decoding B) from the per-row cost
+    r1, r2 = nt, 4 * nt
+    t1, t2 = run(r1), run(r2)
+    per_row = max((t2 - t1) / (r2 - r1), 1e-6)
+    rows = int(min(w.M, max(r2, (target_s - t1 + r1 * per_row) / per_row)))
+    rows = max(nt, rows - rows % nt)
+    dt = run(rows)
     flops = 2.0 * rows * w.N * w.K
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": o.num_threads(),
             "kind": "oracle",
             "sample": f"{rows} of {w.M} rows of C (all {w.N} columns, K={w.K}), {dt:.1f} s"}
+
+
+def parse_tile(spec):
+    """'256x256:2[:1[:8]]' -> the matching compiled configuration."""
+    import software_pipelined_tiled_gemm_amd as spg
+
+    parts = spec.split(":")
+    bm, bn = (int(x) for x in parts[0].lower().split("x"))
+    st = int(parts[1])
+    swz = int(parts[2]) if len(parts) > 2 else 1
+    gm = int(parts[3]) if len(parts) > 3 else 0
+    for i in range(spg.gemm_num_configs()):
+        c = spg.gemm_list_config(i)
+        if (c.block_m, c.block_n, c.stages, c.swizzle) == (bm, bn, st, swz):
+            if gm:
+                c.group_m = gm
+            return c
+    raise SystemExit(f"no compiled configuration matches --tile {spec}")
 
 
 def main():
@@ -96,7 +119,15 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="nn_bf16_8192")
+    ap.add_argument("--workload", default="nn_bf16_8192",
+                    help="workload name from workloads.WORKLOADS")
+    ap.add_argument("--tile", default=None,
+                    help="force a configuration: BMxBN:S[:swizzle[:group_m]] (default: the "
+                         "library's choice)")
+    ap.add_argument("--no-extra", action="store_true", help="skip the fp16 8192^3 extra line")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy 5 times, so that HBM "
+                         "byte counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GEMM is "
@@ -113,19 +144,29 @@ def main():
 
     w = W.WORKLOADS[args.workload]
     log(f"bench: {w.describe()}")
-    wall_ms, kern_ms, cfg = time_gemm(w, args.steps, args.warmup)
+    force = parse_tile(args.tile) if args.tile else None
+    wall_ms, kern_ms, cfg = time_gemm(w, args.steps, args.warmup, force)
     tflops = w.flops / (kern_ms * 1e-3) / 1e12
     wall_tflops = w.flops / (wall_ms * 1e-3) / 1e12
     log(f"  {cfg}: kernel {kern_ms * 1e3:.1f} us ({tflops:.1f} TFLOP/s), "
         f"wall {wall_ms * 1e3:.1f} us/step")
 
     extra = {}
-    if args.workload == "nn_bf16_8192":
+    if args.workload == "nn_bf16_8192" and not args.no_extra:
         w16 = W.WORKLOADS["nn_f16_8192"]
         _, k16, cfg16 = time_gemm(w16, args.steps, args.warmup)
         extra["nn_f16_8192"] = {"tflops": round(w16.flops / (k16 * 1e-3) / 1e12, 2),
                                 "kernel_us": round(k16 * 1e3, 2), "config": cfg16.as_dict()}
         log(f"  fp16 8192^3: {extra['nn_f16_8192']}")
+
+    if args.copy_calibration:
+        src = torch.empty(128 << 20, dtype=torch.int16, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("  copy calibration: 5 x 256 MiB read + 256 MiB written")
+        del src, dst
 
     algo_bytes = 2 * (w.M * w.K + w.K * w.N) + (4 if w.out_dtype == W.F32 else 2) * w.M * w.N
     result = {

@@ -27,10 +27,10 @@ namespace {
 
 typedef void (*launch_fn)(const KArgs&, dim3, hipStream_t);
 
-template <bool BF16, bool B_NK, int BM, int BN, int WM, int WN, int S, bool SWZ>
+template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ>
 void launch_pipelined(const KArgs& a, dim3 grid, hipStream_t st) {
-    using G = spg::Geom<BM, BN, WM, WN, S>;
-    hipLaunchKernelGGL((spg::pipelined_gemm<BF16, B_NK, BM, BN, WM, WN, S, SWZ>), grid,
+    using G = spg::Geom<BM, BN, BK, WM, WN, S>;
+    hipLaunchKernelGGL((spg::pipelined_gemm<BF16, B_NK, BM, BN, BK, WM, WN, S, SWZ>), grid,
                        dim3(G::NT), 0, st, a);
 }
 
@@ -44,27 +44,29 @@ struct Variant {
     launch_fn fn[2][2];  // [bf16][b_nk]
 };
 
-#define SPG_VARIANT(BM, BN, WM, WN, S, SWZ)                                          \
-    Variant{{BM, BN, 64, S, WM, WN, SWZ, 0, 1},                                      \
-            {{launch_pipelined<false, false, BM, BN, WM, WN, S, (SWZ != 0)>,         \
-              launch_pipelined<false, true, BM, BN, WM, WN, S, (SWZ != 0)>},         \
-             {launch_pipelined<true, false, BM, BN, WM, WN, S, (SWZ != 0)>,          \
-              launch_pipelined<true, true, BM, BN, WM, WN, S, (SWZ != 0)>}}}
+#define SPG_VARIANT(BM, BN, BK, WM, WN, S, SWZ)                                          \
+    Variant{{BM, BN, BK, S, WM, WN, SWZ, 0, 1},                                          \
+            {{launch_pipelined<false, false, BM, BN, BK, WM, WN, S, (SWZ != 0)>,         \
+              launch_pipelined<false, true, BM, BN, BK, WM, WN, S, (SWZ != 0)>},         \
+             {launch_pipelined<true, false, BM, BN, BK, WM, WN, S, (SWZ != 0)>,          \
+              launch_pipelined<true, true, BM, BN, BK, WM, WN, S, (SWZ != 0)>}}}
 
-// The compiled configurations.  LDS per workgroup = S * (BM + BN) * 64 * 2 B.
+// The compiled configurations.  LDS per workgroup = S * (BM + BN) * BK * 2 B.
 const Variant kVariants[] = {
-    SPG_VARIANT(256, 256, 128, 128, 2, 1),  // 128 KiB
-    SPG_VARIANT(256, 128, 128, 64, 2, 1),   //  96 KiB
-    SPG_VARIANT(256, 128, 128, 64, 3, 1),   // 144 KiB
-    SPG_VARIANT(128, 256, 64, 128, 2, 1),   //  96 KiB
-    SPG_VARIANT(128, 256, 64, 128, 3, 1),   // 144 KiB
-    SPG_VARIANT(128, 128, 64, 64, 2, 1),    //  64 KiB
-    SPG_VARIANT(128, 128, 64, 64, 3, 1),    //  96 KiB
-    SPG_VARIANT(128, 128, 64, 64, 4, 1),    // 128 KiB
-    // ablations: no overlap (S = 1) and no swizzle
-    SPG_VARIANT(256, 256, 128, 128, 1, 1),  //  64 KiB
-    SPG_VARIANT(256, 256, 128, 128, 2, 0),  // 128 KiB
-    SPG_VARIANT(128, 128, 64, 64, 1, 1),    //  32 KiB
+    SPG_VARIANT(256, 256, 32, 128, 128, 4, 1),  // 128 KiB
+    SPG_VARIANT(256, 256, 32, 128, 128, 5, 1),  // 160 KiB
+    SPG_VARIANT(256, 256, 64, 128, 128, 2, 1),  // 128 KiB
+    SPG_VARIANT(256, 128, 64, 128, 64, 3, 1),   // 144 KiB
+    SPG_VARIANT(256, 128, 32, 128, 64, 6, 1),   // 144 KiB
+    SPG_VARIANT(128, 256, 64, 64, 128, 3, 1),   // 144 KiB
+    SPG_VARIANT(128, 128, 64, 64, 64, 2, 1),    //  64 KiB
+    SPG_VARIANT(128, 128, 64, 64, 64, 3, 1),    //  96 KiB
+    SPG_VARIANT(128, 128, 64, 64, 64, 4, 1),    // 128 KiB
+    // ablations: no overlap (S = 1), no swizzle, 2 stages
+    SPG_VARIANT(256, 256, 64, 128, 128, 1, 1),  //  64 KiB
+    SPG_VARIANT(256, 256, 32, 128, 128, 4, 0),  // 128 KiB
+    SPG_VARIANT(256, 256, 32, 128, 128, 2, 1),  //  64 KiB
+    SPG_VARIANT(128, 128, 64, 64, 64, 1, 1),    //  32 KiB
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 constexpr int kDefaultGroupM = 4;
@@ -137,9 +139,9 @@ gemm_tile_config heuristic(int64_t M, int64_t N) {
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     const int64_t cus = 256;
     gemm_tile_config c;
-    if (tiles(256, 128) >= cus) c = kVariants[2].cfg;
-    else c = kVariants[6].cfg;
-    c.group_m = kDefaultGroupM;
+    if (tiles(256, 256) >= cus) c = kVariants[2].cfg;      // 256x256x64, S=2
+    else c = kVariants[7].cfg;                             // 128x128x64, S=3
+    c.group_m = 8;
     c.xcd_remap = 1;
     return c;
 }

@@ -70,7 +70,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define SPG_LDS __attribute__((address_space(3)))
 
-constexpr int kBK = 64;                  // K extent of one stage: 64 halves = 128 B per row
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past any num_records: loads 0
 
 enum { kOutF16 = 0, kOutBF16 = 1, kOutF32 = 2 };
@@ -92,14 +91,35 @@ struct KArgs {
 // small helpers
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    // word 3 = 0x00020000: 32-bit data format, raw (stride 0) buffer on gfx9
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource (V#) for a raw buffer of `bytes` bytes at `base`: any access at
+// an offset >= bytes returns zero.  Word 3 = 0x00020000 selects the 32-bit data
+// format of a raw (stride 0) buffer on gfx9.  The words are wave-uniform and
+// are forced into SGPRs.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)p);
+    r.y = __builtin_amdgcn_readfirstlane((int32_t)((uint32_t)(p >> 32) & 0xffffu));
+    r.z = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+    r.w = 0x00020000;
+    return r;
 }
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_dst, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SPG_LDS void*)lds_dst, 16, (int)voff, 0, 0, 0);
+// One direct-to-LDS copy of 16 B per lane: the wave's 64 lanes land at LDS bytes
+// [lds_dst, lds_dst + 1024), lane i at lds_dst + 16 i.  Written as inline asm on
+// purpose: the compiler's wait-count pass cannot tell which LDS slot a DMA
+// writes, and would otherwise wait for every outstanding copy before any LDS
+// read, serializing the ring.  The kernel orders these copies itself with
+// s_waitcnt vmcnt(N) and the per-k-tile barrier.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, char* lds_dst, uint32_t voff) {
+    const uint32_t m0 =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(SPG_LDS char*)lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
 }
 
 // Wait until at most N vector-memory instructions of this wave are outstanding.
@@ -111,11 +131,15 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Swizzle of K-contiguous tiles (A, and B stored [N,K]): a row holds 64 halves
-// = 8 chunks of 16 B; logical chunk c of row r lives at chunk c ^ kswz(r).
+// Swizzle of K-contiguous tiles (A, and B stored [N,K]) with BK = 64: a row holds
+// 64 halves = 8 chunks of 16 B; logical chunk c of row r lives at chunk c ^ kswz(r).
 // Rows r..r+7 get distinct XOR values and rows r, r+8 differ in the low bit,
 // so 8 consecutive lanes (one 128-B bank sweep) or 16 (one 256-B sweep) reading
 // the same logical chunk of consecutive rows never share a bank.
+// With BK = 32 a row is 4 chunks (64 B) and the XOR is ((r>>1) ^ (r>>2)) & 3:
+// among 8 aligned rows, the 4 of equal parity (sharing a 128-B sweep) get
+// distinct values, and among 16 aligned rows the 4 of equal r%4 (sharing a
+// 256-B sweep) do too.
 __device__ __forceinline__ int kswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // Swizzle of N-contiguous B tiles ([K,N] storage): the 16-B chunk index of row
@@ -250,45 +274,64 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TN][TM], char* 
     }
 }
 
-template <int BM, int BN, int WM, int WN, int S>
+template <int BM, int BN, int BK, int WM, int WN, int S>
 struct Geom {
     static constexpr int WAVES_N = BN / WN;
     static constexpr int NW = (BM / WM) * WAVES_N;
     static constexpr int NT = NW * 64;
     static constexpr int TM = WM / 32, TN = WN / 32;
-    static constexpr int A_BYTES = BM * kBK * 2;
-    static constexpr int B_BYTES = BN * kBK * 2;
+    static constexpr int KSTEPS = BK / 16;             // MFMA k-steps per k-tile
+    static constexpr int ROWB = BK * 2;                // bytes of a K-contiguous tile row
+    static constexpr int A_BYTES = BM * BK * 2;
+    static constexpr int B_BYTES = BN * BK * 2;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int A_DMA = A_BYTES / 1024 / NW;  // DMA instructions per wave per k-tile
     static constexpr int B_DMA = B_BYTES / 1024 / NW;
     static constexpr int L = A_DMA + B_DMA;
     static constexpr int STG = 32 * WN * 4;            // epilogue staging bytes per wave (fp32 worst case)
+    static_assert(BK == 32 || BK == 64, "BK");
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile shape");
+    static_assert(BN >= 128, "[K,N] swizzle needs 16 chunks per row");
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "DMA split");
-    static_assert(S >= 1 && S <= 4, "stages");
+    static_assert(S >= 1 && S <= 6, "stages");
     static_assert(S * STAGE <= 160 * 1024, "LDS budget");
     static_assert(((NW + S - 1) / S) * STG <= STAGE, "epilogue staging must fit the ring");
     static_assert((S > 2 ? (S - 2) * L : 0) < 64, "vmcnt range");
 };
 
-template <bool BF16, bool B_NK, int BM, int BN, int WM, int WN, int S, bool SWZ>
-__global__ void __launch_bounds__((Geom<BM, BN, WM, WN, S>::NT))
+// Swizzle of a K-contiguous tile row with BK/8 chunks of 16 B (see kswz / kswz4).
+template <int BK>
+__device__ __forceinline__ int kswz_t(int r) {
+    if constexpr (BK == 64) return kswz(r);
+    else return ((r >> 1) ^ (r >> 2)) & 3;
+}
+
+template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ>
+__global__ void __launch_bounds__((Geom<BM, BN, BK, WM, WN, S>::NT))
 pipelined_gemm(KArgs args) {
-    using G = Geom<BM, BN, WM, WN, S>;
-    constexpr int TM = G::TM, TN = G::TN, A_BYTES = G::A_BYTES;
+    using G = Geom<BM, BN, BK, WM, WN, S>;
+    constexpr int TM = G::TM, TN = G::TN, A_BYTES = G::A_BYTES, KSTEPS = G::KSTEPS;
+    constexpr int ROWB = G::ROWB;
     constexpr int A_DMA = G::A_DMA, B_DMA = G::B_DMA;
+    constexpr int CPR_K = BK / 8;          // chunks per K-contiguous row
+    constexpr int RPI_K = 64 / CPR_K;      // K-contiguous rows per DMA instruction
 
     __shared__ __attribute__((aligned(1024))) char ring0[G::STAGE];
     __shared__ __attribute__((aligned(1024))) char ring1[S > 1 ? G::STAGE : 16];
     __shared__ __attribute__((aligned(1024))) char ring2[S > 2 ? G::STAGE : 16];
     __shared__ __attribute__((aligned(1024))) char ring3[S > 3 ? G::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char ring4[S > 4 ? G::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char ring5[S > 5 ? G::STAGE : 16];
 
     // ring slot s as a compile-time choice of array (see the header comment)
     auto slot_of = [&](auto sc) -> char* {
-        if constexpr (decltype(sc)::value == 0) return ring0;
-        else if constexpr (decltype(sc)::value == 1) return ring1;
-        else if constexpr (decltype(sc)::value == 2) return ring2;
-        else return ring3;
+        constexpr int v = decltype(sc)::value;
+        if constexpr (v == 0) return ring0;
+        else if constexpr (v == 1) return ring1;
+        else if constexpr (v == 2) return ring2;
+        else if constexpr (v == 3) return ring3;
+        else if constexpr (v == 4) return ring4;
+        else return ring5;
     };
 
     const int tid = threadIdx.x;
@@ -301,13 +344,12 @@ pipelined_gemm(KArgs args) {
     tile_of(blockIdx.x, args, tm, tn);
     const int M = args.M, N = args.N, K = args.K;
     const int m0 = tm * BM, n0 = tn * BN;
-    const int nk = (K + kBK - 1) / kBK;
+    const int nk = (K + BK - 1) / BK;
 
     // ---- buffer resources: bytes past the end read as zero -------------------
     const int a_rows = (M - m0) < BM ? (M - m0) : BM;
-    const __amdgpu_buffer_rsrc_t rA =
-        make_rsrc(args.A + (size_t)m0 * K, (uint32_t)a_rows * (uint32_t)K * 2u);
-    __amdgpu_buffer_rsrc_t rB;
+    const i32x4 rA = make_rsrc(args.A + (size_t)m0 * K, (uint32_t)a_rows * (uint32_t)K * 2u);
+    i32x4 rB;
     if constexpr (B_NK) {
         const int b_rows = (N - n0) < BN ? (N - n0) : BN;
         rB = make_rsrc(args.B + (size_t)n0 * K, (uint32_t)b_rows * (uint32_t)K * 2u);
@@ -317,14 +359,17 @@ pipelined_gemm(KArgs args) {
     }
 
     // ---- per-lane DMA source offsets (k-tile 0) ------------------------------
+    // DMA instruction d of the tile writes LDS bytes [d*1024, d*1024+1024): lane i
+    // lands at byte i*16, i.e. row d*RPI + i/CPR, physical chunk i%CPR; it fetches
+    // the logical chunk that the swizzle puts there.
     uint32_t offA[A_DMA];
     int colA[A_DMA];
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
         const int d = wave * A_DMA + j;
-        const int r = d * 8 + (lane >> 3);
-        const int p = lane & 7;
-        const int c = SWZ ? (p ^ kswz(r)) : p;
+        const int r = d * RPI_K + lane / CPR_K;
+        const int p = lane % CPR_K;
+        const int c = SWZ ? (p ^ kswz_t<BK>(r)) : p;
         offA[j] = (uint32_t)r * (uint32_t)K * 2u + (uint32_t)c * 16u;
         colA[j] = c * 8;
     }
@@ -334,13 +379,13 @@ pipelined_gemm(KArgs args) {
     for (int j = 0; j < B_DMA; ++j) {
         const int d = wave * B_DMA + j;
         if constexpr (B_NK) {
-            const int r = d * 8 + (lane >> 3);
-            const int p = lane & 7;
-            const int c = SWZ ? (p ^ kswz(r)) : p;
+            const int r = d * RPI_K + lane / CPR_K;
+            const int p = lane % CPR_K;
+            const int c = SWZ ? (p ^ kswz_t<BK>(r)) : p;
             offB[j] = (uint32_t)r * (uint32_t)K * 2u + (uint32_t)c * 16u;
             colB[j] = c * 8;
         } else {
-            constexpr int CPR = BN / 8;          // 16-B chunks per row
+            constexpr int CPR = BN / 8;          // 16-B chunks per [K,N] row
             constexpr int RP = 64 / CPR;         // rows per wave instruction
             const int r = d * RP + lane / CPR;
             const int p = lane % CPR;
@@ -349,51 +394,56 @@ pipelined_gemm(KArgs args) {
             colB[j] = c * 8;
         }
     }
-    const bool k_tail = (K % kBK) != 0;
+    const bool k_tail = (K % BK) != 0;
     const bool n_tail = !B_NK && (n0 + BN > N);
 
-    auto issue = [&](char* slot, int kt) __attribute__((always_inline)) {
-        const int k0 = kt * kBK;
-        const bool last = k_tail && (kt == nk - 1);
-#pragma unroll
-        for (int j = 0; j < A_DMA; ++j) {
+    // DMA op j (compile-time) of k-tile kt into `slot`: j < A_DMA copies A rows,
+    // the rest B.  On the last k-tile, chunks past K (or columns past N for a
+    // [K,N] B) are redirected past the buffer end and read as zero.
+    auto dma_op = [&](char* slot, int kt, auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        const int k0 = kt * BK;
+        if constexpr (j < A_DMA) {
             uint32_t off = offA[j] + (uint32_t)k0 * 2u;
-            if (last && k0 + colA[j] + 8 > K) off = kOOB;
+            if (k_tail && kt == nk - 1 && k0 + colA[j] + 8 > K) off = kOOB;
             dma16(rA, slot + (wave * A_DMA + j) * 1024, off);
-        }
-#pragma unroll
-        for (int j = 0; j < B_DMA; ++j) {
+        } else {
+            constexpr int jb = j - A_DMA;
             uint32_t off;
             if constexpr (B_NK) {
-                off = offB[j] + (uint32_t)k0 * 2u;
-                if (last && k0 + colB[j] + 8 > K) off = kOOB;
+                off = offB[jb] + (uint32_t)k0 * 2u;
+                if (k_tail && kt == nk - 1 && k0 + colB[jb] + 8 > K) off = kOOB;
             } else {
-                off = offB[j] + (uint32_t)k0 * (uint32_t)N * 2u;
-                if (n_tail && n0 + colB[j] + 8 > N) off = kOOB;
+                off = offB[jb] + (uint32_t)k0 * (uint32_t)N * 2u;
+                if (n_tail && n0 + colB[jb] + 8 > N) off = kOOB;
             }
-            dma16(rB, slot + A_BYTES + (wave * B_DMA + j) * 1024, off);
+            dma16(rB, slot + A_BYTES + (wave * B_DMA + jb) * 1024, off);
         }
+    };
+    auto issue = [&](char* slot, int kt) __attribute__((always_inline)) {
+        static_for<0, G::L>([&](auto jc) { dma_op(slot, kt, jc); });
     };
 
     // ---- per-lane LDS read offsets -------------------------------------------
     // A (second MFMA operand): lane l reads row wm*WM + bm*32 + l%32,
-    // k = kk*16 + (l/32)*8 .. +7  (16-B chunk 2kk + l/32).
-    int aoff[4];
+    // k = kk*16 + (l/32)*8 .. +7  (16-B chunk 2kk + l/32).  The swizzle depends on
+    // the row's low 4 bits only, which are those of l%32.
+    int aoff[KSTEPS];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < KSTEPS; ++kk) {
         const int c = kk * 2 + (lane >> 5);
         const int r = lane & 31;
-        aoff[kk] = (wm * WM + r) * 128 + (SWZ ? (c ^ kswz(r)) : c) * 16;
+        aoff[kk] = (wm * WM + r) * ROWB + (SWZ ? (c ^ kswz_t<BK>(r)) : c) * 16;
     }
     // B (first MFMA operand): lane l needs column n = wn*WN + bn*32 + l%32 with the
     // same 8 k values as A.
-    int boff[B_NK ? 4 : TN];
+    int boff[B_NK ? KSTEPS : TN];
     if constexpr (B_NK) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < KSTEPS; ++kk) {
             const int c = kk * 2 + (lane >> 5);
             const int r = lane & 31;
-            boff[kk] = A_BYTES + (wn * WN + r) * 128 + (SWZ ? (c ^ kswz(r)) : c) * 16;
+            boff[kk] = A_BYTES + (wn * WN + r) * ROWB + (SWZ ? (c ^ kswz_t<BK>(r)) : c) * 16;
         }
     } else {
         // ds_read_b64_tr_b16: in each 16-lane group, lane i supplies 8 B of row
@@ -423,25 +473,29 @@ pipelined_gemm(KArgs args) {
         u32x4 a[TM];
         u32x4 b[TN];
     };
-    auto load_frags = [&](const char* slot, int kk, Frags& f) __attribute__((always_inline)) {
-#pragma unroll
-        for (int bm = 0; bm < TM; ++bm)
-            f.a[bm] = *(const SPG_LDS u32x4*)(slot + aoff[kk] + bm * 32 * 128);
-#pragma unroll
-        for (int bn = 0; bn < TN; ++bn) {
-            if constexpr (B_NK) {
-                f.b[bn] = *(const SPG_LDS u32x4*)(slot + boff[kk] + bn * 32 * 128);
-            } else {
-                constexpr int RB = BN * 2;
-                const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (SPG_LDS shortx4*)(slot + boff[bn] + (kk * 16) * RB));
-                const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (SPG_LDS shortx4*)(slot + boff[bn] + (kk * 16 + 4) * RB));
-                const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-                const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-                f.b[bn] = u32x4{l2[0], l2[1], h2[0], h2[1]};
-            }
+    // LDS read op r (compile-time) of stage kk into f: r < TM are the A rows, then
+    // the B columns (one ds_read_b128 each for [N,K] storage, two transposing
+    // reads -- k 0..3 and 4..7 of the lane's 8 -- for [K,N] storage).
+    constexpr int NRD = TM + (B_NK ? TN : 2 * TN);
+    auto read_op = [&](const char* slot, int kk, Frags& f, auto rc) __attribute__((always_inline)) {
+        constexpr int r = decltype(rc)::value;
+        if constexpr (r < TM) {
+            f.a[r] = *(const SPG_LDS u32x4*)(slot + aoff[kk] + r * 32 * ROWB);
+        } else if constexpr (B_NK) {
+            constexpr int bn = r - TM;
+            f.b[bn] = *(const SPG_LDS u32x4*)(slot + boff[kk] + bn * 32 * ROWB);
+        } else {
+            constexpr int bn = (r - TM) / 2, h = (r - TM) % 2;
+            constexpr int RB = BN * 2;
+            const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (SPG_LDS shortx4*)(slot + boff[bn] + (kk * 16 + h * 4) * RB));
+            const u32x2 v2 = __builtin_bit_cast(u32x2, v);
+            f.b[bn][2 * h] = v2[0];
+            f.b[bn][2 * h + 1] = v2[1];
         }
+    };
+    auto load_frags = [&](const char* slot, int kk, Frags& f) __attribute__((always_inline)) {
+        static_for<0, NRD>([&](auto rc) { read_op(slot, kk, f, rc); });
     };
     auto mma = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
@@ -453,18 +507,53 @@ pipelined_gemm(KArgs args) {
     // keep each stage's loads and MFMAs together: no motion across stage boundaries
     auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
 
+    // One MFMA stage with its memory traffic interleaved: step i issues MFMA i of
+    // `now`, then LDS read i of the next stage (into `nx`, from `rslot` at k-step
+    // rkk) and, when `dslot` is given, DMA op i of k-tile `dkt`.  A scheduling
+    // barrier after every step keeps this order, so the single wave of each SIMD
+    // hands the matrix pipe a new MFMA every step while the LDS and the copies are
+    // fed in its shadow instead of in bursts.
+    constexpr int NMMA = TN * TM;
+    auto stage = [&](const Frags& now, const char* rslot, int rkk, Frags& nx, char* dslot,
+                     int dkt, auto do_read, auto do_dma) __attribute__((always_inline)) {
+        constexpr bool RD = decltype(do_read)::value, DM = decltype(do_dma)::value;
+        constexpr int STEPS = NMMA > NRD ? (NMMA > G::L ? NMMA : G::L) : (NRD > G::L ? NRD : G::L);
+        static_for<0, STEPS>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i < NMMA) {
+                constexpr int bn = i / TM, bm = i % TM;
+                acc[bn][bm] = mfma<BF16>(now.b[bn], now.a[bm], acc[bn][bm]);
+            }
+            if constexpr (DM && i < G::L) dma_op(dslot, dkt, std::integral_constant<int, i>{});
+            if constexpr (RD && i < NRD) read_op(rslot, rkk, nx, std::integral_constant<int, i>{});
+            fence();
+        });
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+
+    Frags f0, f1;
+
     // ---- the pipelined K loop ----------------------------------------------------
     //
-    // One k-tile = 4 MFMA stages (kk = 0..3, 16 k each).  Stage kk issues the LDS
-    // reads of stage kk+1 and then the MFMAs of stage kk.  Between stages 2 and 3 --
-    // after this wave's last LDS read of the current slot -- sits the one barrier of
-    // the k-tile: once every wave has passed it, (a) the next k-tile, whose DMA this
+    // One k-tile = KSTEPS MFMA stages of 16 k.  Stage kk reads the fragments of
+    // stage kk+1 while the MFMAs of stage kk run.  Before the last stage -- after
+    // this wave's last LDS read of the current slot -- sits the one barrier of the
+    // k-tile: once every wave has passed it, (a) the next k-tile, whose DMA this
     // wave has waited for, is visible to all, and (b) nobody reads the current slot
     // any more, so it is released and refilled with k-tile t+S while the MFMAs of
-    // stage 3 (which read registers, not LDS) still run.  Stage 3 also issues the
-    // first LDS reads of the next k-tile, so the matrix pipe has work across the
-    // k-tile boundary.
-    Frags f0, f1;
+    // the last stage (which read registers, not LDS) still run.  The last stage
+    // also reads the first fragments of the next k-tile, so the matrix pipe has
+    // work across the k-tile boundary.  KSTEPS is even, so stage kk computes from
+    // f0 when kk is even and the last stage from f1.
+    static_assert(KSTEPS % 2 == 0, "fragment double buffer assumes an even k-step count");
+    auto first_stages = [&](const char* cur) __attribute__((always_inline)) {
+        static_for<0, KSTEPS - 1>([&](auto kc) {
+            constexpr int kk = decltype(kc)::value;
+            if constexpr (kk % 2 == 0) stage(f0, cur, kk + 1, f1, nullptr, 0, T_{}, F_{});
+            else stage(f1, cur, kk + 1, f0, nullptr, 0, T_{}, F_{});
+        });
+    };
     if constexpr (S == 1) {
         // the serial K loop: copy, wait, multiply, and only then let the next copy in
         for (int t = 0; t < nk; ++t) {
@@ -472,17 +561,8 @@ pipelined_gemm(KArgs args) {
             wait_vmcnt<0>();
             __syncthreads();
             load_frags(ring0, 0, f0);
-            load_frags(ring0, 1, f1);
-            fence();
-            mma(f0);
-            load_frags(ring0, 2, f0);
-            fence();
-            mma(f1);
-            load_frags(ring0, 3, f1);
-            fence();
-            mma(f0);
-            fence();
-            mma(f1);
+            first_stages(ring0);
+            stage(f1, nullptr, 0, f0, nullptr, 0, F_{}, F_{});
             __syncthreads();
         }
     } else {
@@ -496,48 +576,46 @@ pipelined_gemm(KArgs args) {
         load_frags(ring0, 0, f0);
 
         constexpr int STEADY = (S - 2) * G::L;
-        // k-tile t (< nk) in slot s.  FULL (compile-time) means t+S < nk: the k-tiles
-        // t+1 .. t+S-1 are all in flight, exactly the copies of t+2 .. t+S-1 may stay
-        // outstanding, and slot s is refilled with k-tile t+S.  Otherwise the same
-        // decisions are taken at run time; only the boundary (wait, barrier, refill,
-        // next reads) is conditional, never the MFMAs.
-        auto ktile = [&](auto sc, int t, auto full) __attribute__((always_inline)) {
+        // k-tile t (< nk) in slot s, steady state (t+S < nk): the k-tiles t+1 .. t+S-1
+        // are all in flight, exactly the copies of t+2 .. t+S-1 may stay outstanding,
+        // and slot s is refilled with k-tile t+S during the last stage.
+        auto ktile_full = [&](auto sc, int t) __attribute__((always_inline)) {
             constexpr int s = decltype(sc)::value;
-            constexpr bool FULL = decltype(full)::value;
-            const char* cur = slot_of(sc);
+            char* cur = slot_of(sc);
             const char* nxt = slot_of(std::integral_constant<int, (s + 1) % S>{});
-            load_frags(cur, 1, f1);
-            fence();
-            mma(f0);
-            load_frags(cur, 2, f0);
-            fence();
-            mma(f1);
-            load_frags(cur, 3, f1);
-            fence();
-            mma(f0);
-            fence();
-            if (FULL || t + 1 < nk) {
-                if (FULL || t + S < nk) wait_vmcnt<STEADY>();
+            first_stages(cur);
+            wait_vmcnt<STEADY>();
+            __syncthreads();
+            stage(f1, nxt, 0, f0, cur, t + S, T_{}, T_{});
+        };
+        // k-tile t (< nk) near the end: the same decisions taken at run time.  Only the
+        // boundary (wait, barrier, refill, next reads) is conditional, never the MFMAs.
+        auto ktile_tail = [&](auto sc, int t) __attribute__((always_inline)) {
+            constexpr int s = decltype(sc)::value;
+            char* cur = slot_of(sc);
+            const char* nxt = slot_of(std::integral_constant<int, (s + 1) % S>{});
+            first_stages(cur);
+            if (t + 1 < nk) {
+                if (t + S < nk) wait_vmcnt<STEADY>();
                 else wait_vmcnt<0>();
                 __syncthreads();
-                if (FULL || t + S < nk) issue(slot_of(sc), t + S);
+                if (t + S < nk) issue(cur, t + S);
                 load_frags(nxt, 0, f0);
             }
             fence();
             mma(f1);
+            fence();
         };
         // steady state: S k-tiles per iteration, static slots, no branches
         int t0 = 0;
         for (; t0 + 2 * S <= nk; t0 += S) {
-            static_for<0, S>([&](auto sc) {
-                ktile(sc, t0 + decltype(sc)::value, std::true_type{});
-            });
+            static_for<0, S>([&](auto sc) { ktile_full(sc, t0 + decltype(sc)::value); });
         }
         // drain: fewer than 2S k-tiles remain; t0 is a multiple of S
         static_for<0, 2 * S - 1>([&](auto sc) {
             constexpr int i = decltype(sc)::value;
             const int t = t0 + i;
-            if (t < nk) ktile(std::integral_constant<int, i % S>{}, t, std::false_type{});
+            if (t < nk) ktile_tail(std::integral_constant<int, i % S>{}, t);
         });
     }
 
@@ -546,7 +624,8 @@ pipelined_gemm(KArgs args) {
     char* stg;
     {
         const int sl = wave % S;
-        char* base = sl == 0 ? ring0 : sl == 1 ? ring1 : sl == 2 ? ring2 : ring3;
+        char* base = sl == 0 ? ring0 : sl == 1 ? ring1 : sl == 2 ? ring2 : sl == 3 ? ring3
+                   : sl == 4 ? ring4 : ring5;
         stg = base + (wave / S) * G::STG;
     }
     // one branch on the (uniform) output type and epilogue, outside all accumulator reads
