@@ -95,18 +95,52 @@ def cpu_baseline(w, target_s=15.0):
             "sample": f"{rows} of {w.M} rows of C (all {w.N} columns, K={w.K}), {dt:.1f} s"}
 
 
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources (same recipe as the profile summaries record)."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "software_pipelined_tiled_gemm_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, forced: bool):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
+    or None when the kernel sources changed since the counters were taken (or the
+    configuration is not the default one they were taken on)."""
+    path = os.path.join(ROOT, "profiles", f"pipelined_gemm_{workload}_counters.md")
+    if forced or not os.path.exists(path):
+        return None
+    src, traffic = None, None
+    for line in open(path):
+        if "kernel sources sha256:" in line:
+            src = line.split(":", 1)[1].strip()
+        if "traffic_bytes_per_launch:" in line:
+            traffic = float(line.split(":", 1)[1].strip())
+    if src != kernel_source_hash():
+        return None
+    return traffic
+
+
 def parse_tile(spec):
-    """'256x256:2[:1[:8]]' -> the matching compiled configuration."""
+    """'256x256x64:2[:swizzle[:group_m[:staging]]]' -> the matching compiled configuration."""
     import software_pipelined_tiled_gemm_amd as spg
 
     parts = spec.split(":")
-    bm, bn = (int(x) for x in parts[0].lower().split("x"))
+    dims = [int(x) for x in parts[0].lower().split("x")]
+    bm, bn = dims[0], dims[1]
+    bk = dims[2] if len(dims) > 2 else 64
     st = int(parts[1])
     swz = int(parts[2]) if len(parts) > 2 else 1
     gm = int(parts[3]) if len(parts) > 3 else 0
+    stg = int(parts[4]) if len(parts) > 4 else 0
     for i in range(spg.gemm_num_configs()):
         c = spg.gemm_list_config(i)
-        if (c.block_m, c.block_n, c.stages, c.swizzle) == (bm, bn, st, swz):
+        if (c.block_m, c.block_n, c.block_k, c.stages, c.swizzle, c.staging) == (bm, bn, bk, st, swz, stg):
             if gm:
                 c.group_m = gm
             return c
@@ -122,8 +156,8 @@ def main():
     ap.add_argument("--workload", default="nn_bf16_8192",
                     help="workload name from workloads.WORKLOADS")
     ap.add_argument("--tile", default=None,
-                    help="force a configuration: BMxBN:S[:swizzle[:group_m]] (default: the "
-                         "library's choice)")
+                    help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging]]] "
+                         "(default: the library's choice)")
     ap.add_argument("--no-extra", action="store_true", help="skip the fp16 8192^3 extra line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy 5 times, so that HBM "
@@ -190,7 +224,8 @@ def main():
         "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS[w.in_dtype], 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": PEAK_TFLOPS[w.in_dtype], "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_TFLOPS[w.in_dtype], 4), "traffic": None,
+                     "frac": round(tflops / PEAK_TFLOPS[w.in_dtype], 4),
+                     "traffic": measured_traffic(w.name, force is not None),
                      "algorithmic_bytes": algo_bytes},
         "extra": extra,
     }

@@ -67,6 +67,9 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1 } gemm_epilogue;
  *   swizzle             1 = XOR-swizzled LDS layout, 0 = plain row layout (ablation)
  *   group_m             tile-raster group height in tiles (L2 reuse); 0 = default
  *   xcd_remap           1 = give each of the 8 XCDs a contiguous range of tiles
+ *   staging             0 = k-tiles are copied straight from memory into LDS
+ *                       (buffer_load ... lds); 1 = copied into VGPRs one k-tile ahead
+ *                       and written to LDS with ds_write_b128
  * The LDS a configuration needs is stages * (block_m + block_n) * block_k * 2 bytes
  * (the shared-memory bound of the TileLang tutorial's shared_bytes()), at most 160 KiB. */
 typedef struct {
@@ -76,6 +79,7 @@ typedef struct {
     int32_t swizzle;
     int32_t group_m;
     int32_t xcd_remap;
+    int32_t staging;
 } gemm_tile_config;
 
 typedef struct gemm_plan* gemm_handle;

@@ -37,7 +37,7 @@ class TileConfig(ctypes.Structure):
                 ("block_k", ctypes.c_int32), ("stages", ctypes.c_int32),
                 ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32),
                 ("swizzle", ctypes.c_int32), ("group_m", ctypes.c_int32),
-                ("xcd_remap", ctypes.c_int32)]
+                ("xcd_remap", ctypes.c_int32), ("staging", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: int(getattr(self, k)) for k, _ in self._fields_}
@@ -53,7 +53,8 @@ class TileConfig(ctypes.Structure):
         d = self.as_dict()
         return (f"TileConfig({d['block_m']}x{d['block_n']}x{d['block_k']}, S={d['stages']}, "
                 f"wave {d['wave_m']}x{d['wave_n']}, swizzle={d['swizzle']}, "
-                f"group_m={d['group_m']}, xcd_remap={d['xcd_remap']})")
+                f"group_m={d['group_m']}, xcd_remap={d['xcd_remap']}, "
+                f"staging={'vgpr' if d['staging'] else 'direct'})")
 
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_get_config", "gemm_autotune",

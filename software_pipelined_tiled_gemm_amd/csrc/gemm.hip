@@ -19,20 +19,13 @@
 #include <tuple>
 #include <vector>
 
-#include "gemm_kernels.hpp"
+#include "launch.hpp"
 
 using spg::KArgs;
+using spg::launch_fn;
+using spg::launch_pipelined;
 
 namespace {
-
-typedef void (*launch_fn)(const KArgs&, dim3, hipStream_t);
-
-template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ>
-void launch_pipelined(const KArgs& a, dim3 grid, hipStream_t st) {
-    using G = spg::Geom<BM, BN, BK, WM, WN, S>;
-    hipLaunchKernelGGL((spg::pipelined_gemm<BF16, B_NK, BM, BN, BK, WM, WN, S, SWZ>), grid,
-                       dim3(G::NT), 0, st, a);
-}
 
 template <bool BF16, bool B_NK>
 void launch_simple(const KArgs& a, dim3 grid, hipStream_t st) {
@@ -44,30 +37,17 @@ struct Variant {
     launch_fn fn[2][2];  // [bf16][b_nk]
 };
 
-#define SPG_VARIANT(BM, BN, BK, WM, WN, S, SWZ)                                          \
-    Variant{{BM, BN, BK, S, WM, WN, SWZ, 0, 1},                                          \
-            {{launch_pipelined<false, false, BM, BN, BK, WM, WN, S, (SWZ != 0)>,         \
-              launch_pipelined<false, true, BM, BN, BK, WM, WN, S, (SWZ != 0)>},         \
-             {launch_pipelined<true, false, BM, BN, BK, WM, WN, S, (SWZ != 0)>,          \
-              launch_pipelined<true, true, BM, BN, BK, WM, WN, S, (SWZ != 0)>}}}
+#define SPG_V(unit, BM, BN, BK, WM, WN, S, SWZ, LDM)                                       \
+    Variant{{BM, BN, BK, S, WM, WN, SWZ, 0, 1, LDM},                                       \
+            {{launch_pipelined<false, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM>,      \
+              launch_pipelined<false, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM>},      \
+             {launch_pipelined<true, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM>,       \
+              launch_pipelined<true, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM>}}},
 
-// The compiled configurations.  LDS per workgroup = S * (BM + BN) * BK * 2 B.
 const Variant kVariants[] = {
-    SPG_VARIANT(256, 256, 32, 128, 128, 4, 1),  // 128 KiB
-    SPG_VARIANT(256, 256, 32, 128, 128, 5, 1),  // 160 KiB
-    SPG_VARIANT(256, 256, 64, 128, 128, 2, 1),  // 128 KiB
-    SPG_VARIANT(256, 128, 64, 128, 64, 3, 1),   // 144 KiB
-    SPG_VARIANT(256, 128, 32, 128, 64, 6, 1),   // 144 KiB
-    SPG_VARIANT(128, 256, 64, 64, 128, 3, 1),   // 144 KiB
-    SPG_VARIANT(128, 128, 64, 64, 64, 2, 1),    //  64 KiB
-    SPG_VARIANT(128, 128, 64, 64, 64, 3, 1),    //  96 KiB
-    SPG_VARIANT(128, 128, 64, 64, 64, 4, 1),    // 128 KiB
-    // ablations: no overlap (S = 1), no swizzle, 2 stages
-    SPG_VARIANT(256, 256, 64, 128, 128, 1, 1),  //  64 KiB
-    SPG_VARIANT(256, 256, 32, 128, 128, 4, 0),  // 128 KiB
-    SPG_VARIANT(256, 256, 32, 128, 128, 2, 1),  //  64 KiB
-    SPG_VARIANT(128, 128, 64, 64, 64, 1, 1),    //  32 KiB
+#include "variants.inc"
 };
+#undef SPG_V
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 constexpr int kDefaultGroupM = 4;
 
@@ -92,7 +72,7 @@ std::map<ProblemKey, gemm_tile_config> g_tuned;
 bool same_tile(const gemm_tile_config& a, const gemm_tile_config& b) {
     return a.block_m == b.block_m && a.block_n == b.block_n && a.block_k == b.block_k &&
            a.stages == b.stages && a.wave_m == b.wave_m && a.wave_n == b.wave_n &&
-           a.swizzle == b.swizzle;
+           a.swizzle == b.swizzle && a.staging == b.staging;
 }
 
 const Variant* find_variant(const gemm_tile_config& c) {
@@ -133,14 +113,22 @@ bool pipelined_fits(int64_t M, int64_t N, int64_t K, gemm_b_layout bl) {
     return true;
 }
 
+const Variant* find_cfg(int bm, int bn, int bk, int stages, int staging) {
+    for (const Variant& v : kVariants)
+        if (v.cfg.block_m == bm && v.cfg.block_n == bn && v.cfg.block_k == bk &&
+            v.cfg.stages == stages && v.cfg.staging == staging && v.cfg.swizzle == 1)
+            return &v;
+    return nullptr;
+}
+
 gemm_tile_config heuristic(int64_t M, int64_t N) {
     // Prefer the largest tile (least L2->LDS traffic per flop) that still gives
     // every CU at least one tile; MI355X has 256 CUs.
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     const int64_t cus = 256;
     gemm_tile_config c;
-    if (tiles(256, 256) >= cus) c = kVariants[2].cfg;      // 256x256x64, S=2
-    else c = kVariants[7].cfg;                             // 128x128x64, S=3
+    if (tiles(256, 256) >= cus) c = find_cfg(256, 256, 64, 2, 0)->cfg;
+    else c = find_cfg(128, 128, 64, 3, 0)->cfg;
     c.group_m = 8;
     c.xcd_remap = 1;
     return c;
@@ -235,7 +223,8 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
         if (force->block_m <= 0 || force->block_n <= 0 || force->block_k <= 0 ||
             force->stages <= 0 || force->wave_m <= 0 || force->wave_n <= 0 ||
             force->group_m < 0 || (force->swizzle != 0 && force->swizzle != 1) ||
-            (force->xcd_remap != 0 && force->xcd_remap != 1))
+            (force->xcd_remap != 0 && force->xcd_remap != 1) ||
+            (force->staging != 0 && force->staging != 1))
             return GEMM_ERR_INVALID_ARG;
         if (gemm_lds_bytes(force) > 160 * 1024) return GEMM_ERR_UNSUPPORTED;
         var = find_variant(*force);
@@ -281,7 +270,7 @@ gemm_status gemm_get_config(gemm_handle h, gemm_tile_config* out) {
     if (!h || !out) return GEMM_ERR_INVALID_ARG;
     *out = h->cfg;
     if (h->simple) {
-        *out = gemm_tile_config{64, 64, 0, 1, 64, 64, 0, 1, 0};
+        *out = gemm_tile_config{64, 64, 0, 1, 64, 64, 0, 1, 0, 0};
     }
     return GEMM_OK;
 }

@@ -274,6 +274,18 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TN][TM], char* 
     }
 }
 
+// Workgroup barrier for LDS hazards only: this wave's LDS operations have
+// completed (lgkmcnt(0)) and every wave has arrived.  Unlike __syncthreads it
+// does not wait for outstanding global loads, so staged loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_b(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int S>
 struct Geom {
     static constexpr int WAVES_N = BN / WN;
@@ -306,7 +318,12 @@ __device__ __forceinline__ int kswz_t(int r) {
     else return ((r >> 1) ^ (r >> 2)) & 3;
 }
 
-template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ>
+// LDM selects how a k-tile reaches its LDS slot:
+//   0  direct-to-LDS copies (buffer_load ... lds), no VGPR staging;
+//   1  register-staged: buffer_load_dwordx4 into VGPRs one k-tile ahead, then
+//      ds_write_b128 into the same swizzled slot layout.  LDS writes from VGPRs
+//      leave the LDS more read bandwidth than direct copies do.
+template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ, int LDM>
 __global__ void __launch_bounds__((Geom<BM, BN, BK, WM, WN, S>::NT))
 pipelined_gemm(KArgs args) {
     using G = Geom<BM, BN, BK, WM, WN, S>;
@@ -348,15 +365,23 @@ pipelined_gemm(KArgs args) {
 
     // ---- buffer resources: bytes past the end read as zero -------------------
     const int a_rows = (M - m0) < BM ? (M - m0) : BM;
-    const i32x4 rA = make_rsrc(args.A + (size_t)m0 * K, (uint32_t)a_rows * (uint32_t)K * 2u);
-    i32x4 rB;
+    const void* a_base = args.A + (size_t)m0 * K;
+    const uint32_t a_bytes = (uint32_t)a_rows * (uint32_t)K * 2u;
+    const void* b_base;
+    uint32_t b_bytes;
     if constexpr (B_NK) {
         const int b_rows = (N - n0) < BN ? (N - n0) : BN;
-        rB = make_rsrc(args.B + (size_t)n0 * K, (uint32_t)b_rows * (uint32_t)K * 2u);
+        b_base = args.B + (size_t)n0 * K;
+        b_bytes = (uint32_t)b_rows * (uint32_t)K * 2u;
     } else {
         // rows k >= K fall past num_records; columns past N are masked per lane
-        rB = make_rsrc(args.B + n0, (uint32_t)(((size_t)K * N - n0) * 2u));
+        b_base = args.B + n0;
+        b_bytes = (uint32_t)(((size_t)K * N - n0) * 2u);
     }
+    const i32x4 rA = make_rsrc(a_base, a_bytes);
+    const i32x4 rB = make_rsrc(b_base, b_bytes);
+    const __amdgpu_buffer_rsrc_t rAb = make_rsrc_b(a_base, a_bytes);
+    const __amdgpu_buffer_rsrc_t rBb = make_rsrc_b(b_base, b_bytes);
 
     // ---- per-lane DMA source offsets (k-tile 0) ------------------------------
     // DMA instruction d of the tile writes LDS bytes [d*1024, d*1024+1024): lane i
@@ -397,19 +422,19 @@ pipelined_gemm(KArgs args) {
     const bool k_tail = (K % BK) != 0;
     const bool n_tail = !B_NK && (n0 + BN > N);
 
-    // DMA op j (compile-time) of k-tile kt into `slot`: j < A_DMA copies A rows,
-    // the rest B.  On the last k-tile, chunks past K (or columns past N for a
-    // [K,N] B) are redirected past the buffer end and read as zero.
-    auto dma_op = [&](char* slot, int kt, auto jc) __attribute__((always_inline)) {
+    // Copy op j (compile-time) of k-tile kt: j < A_DMA moves A rows, the rest B.
+    // Each moves 16 B per lane into LDS bytes lds_off(j) + 16*lane of the slot.
+    // On the last k-tile, chunks past K (or columns past N for a [K,N] B) are
+    // redirected past the buffer end and read as zero.
+    auto src_off = [&](int kt, auto jc) __attribute__((always_inline)) -> uint32_t {
         constexpr int j = decltype(jc)::value;
         const int k0 = kt * BK;
+        uint32_t off;
         if constexpr (j < A_DMA) {
-            uint32_t off = offA[j] + (uint32_t)k0 * 2u;
+            off = offA[j] + (uint32_t)k0 * 2u;
             if (k_tail && kt == nk - 1 && k0 + colA[j] + 8 > K) off = kOOB;
-            dma16(rA, slot + (wave * A_DMA + j) * 1024, off);
         } else {
             constexpr int jb = j - A_DMA;
-            uint32_t off;
             if constexpr (B_NK) {
                 off = offB[jb] + (uint32_t)k0 * 2u;
                 if (k_tail && kt == nk - 1 && k0 + colB[jb] + 8 > K) off = kOOB;
@@ -417,8 +442,28 @@ pipelined_gemm(KArgs args) {
                 off = offB[jb] + (uint32_t)k0 * (uint32_t)N * 2u;
                 if (n_tail && n0 + colB[jb] + 8 > N) off = kOOB;
             }
-            dma16(rB, slot + A_BYTES + (wave * B_DMA + jb) * 1024, off);
         }
+        return kt < nk ? off : kOOB;  // past the last k-tile: zeros
+    };
+    auto lds_off = [&](auto jc) __attribute__((always_inline)) -> int {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (j < A_DMA) return (wave * A_DMA + j) * 1024;
+        else return A_BYTES + (wave * B_DMA + (j - A_DMA)) * 1024;
+    };
+    auto dma_op = [&](char* slot, int kt, auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        dma16(j < A_DMA ? rA : rB, slot + lds_off(jc), src_off(kt, jc));
+    };
+    // register staging (LDM 1): one k-tile of copies in flight in VGPRs
+    u32x4 stage_regs[G::L];
+    auto gload_op = [&](int kt, auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        stage_regs[j] = __builtin_amdgcn_raw_buffer_load_b128(j < A_DMA ? rAb : rBb,
+                                                        (int)src_off(kt, jc), 0, 0);
+    };
+    auto lwrite_op = [&](char* slot, auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        *(SPG_LDS u32x4*)(slot + lds_off(jc) + lane * 16) = stage_regs[j];
     };
     auto issue = [&](char* slot, int kt) __attribute__((always_inline)) {
         static_for<0, G::L>([&](auto jc) { dma_op(slot, kt, jc); });
@@ -514,23 +559,44 @@ pipelined_gemm(KArgs args) {
     // hands the matrix pipe a new MFMA every step while the LDS and the copies are
     // fed in its shadow instead of in bursts.
     constexpr int NMMA = TN * TM;
-    auto stage = [&](const Frags& now, const char* rslot, int rkk, Frags& nx, char* dslot,
-                     int dkt, auto do_read, auto do_dma) __attribute__((always_inline)) {
-        constexpr bool RD = decltype(do_read)::value, DM = decltype(do_dma)::value;
-        constexpr int STEPS = NMMA > NRD ? (NMMA > G::L ? NMMA : G::L) : (NRD > G::L ? NRD : G::L);
+    constexpr int CPS = G::L / KSTEPS;  // register-staged copy ops per MFMA stage
+    static_assert(G::L % KSTEPS == 0, "copy ops must split evenly over the stages");
+    // One MFMA stage with its memory traffic interleaved: step i issues MFMA i of
+    // `now`, then LDS read i of the next stage (into `nx`, from `rslot` at k-step
+    // rkk) and copy op i.  MODE 1: direct-to-LDS copy op i of k-tile ckt into
+    // cslot; MODE 2: copy ops J0.. J0+CPS-1 of the register-staged pipeline (write
+    // the staged data into cslot, then load k-tile ckt into the freed registers).
+    // A scheduling barrier after every step keeps this order, so the single wave
+    // of each SIMD hands the matrix pipe a new MFMA every step while the LDS and
+    // the copies are fed in its shadow instead of in bursts.
+    auto stage = [&](const Frags& now, const char* rslot, int rkk, Frags& nx, char* cslot,
+                     int ckt, auto do_read, auto mode, auto j0c) __attribute__((always_inline)) {
+        constexpr bool RD = decltype(do_read)::value;
+        constexpr int MD = decltype(mode)::value;
+        constexpr int J0 = decltype(j0c)::value;
+        constexpr int NCP = MD == 1 ? G::L : (MD == 2 ? CPS : 0);
+        constexpr int STEPS = NMMA > NRD ? (NMMA > NCP ? NMMA : NCP) : (NRD > NCP ? NRD : NCP);
         static_for<0, STEPS>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             if constexpr (i < NMMA) {
                 constexpr int bn = i / TM, bm = i % TM;
                 acc[bn][bm] = mfma<BF16>(now.b[bn], now.a[bm], acc[bn][bm]);
             }
-            if constexpr (DM && i < G::L) dma_op(dslot, dkt, std::integral_constant<int, i>{});
+            if constexpr (MD == 1 && i < NCP) dma_op(cslot, ckt, std::integral_constant<int, i>{});
+            if constexpr (MD == 2 && i < NCP) {
+                lwrite_op(cslot, std::integral_constant<int, J0 + i>{});
+                gload_op(ckt, std::integral_constant<int, J0 + i>{});
+            }
             if constexpr (RD && i < NRD) read_op(rslot, rkk, nx, std::integral_constant<int, i>{});
             fence();
         });
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
+    using M0_ = std::integral_constant<int, 0>;
+    using M1_ = std::integral_constant<int, 1>;
+    using M2_ = std::integral_constant<int, 2>;
+    using Z_ = std::integral_constant<int, 0>;
 
     Frags f0, f1;
 
@@ -550,8 +616,8 @@ pipelined_gemm(KArgs args) {
     auto first_stages = [&](const char* cur) __attribute__((always_inline)) {
         static_for<0, KSTEPS - 1>([&](auto kc) {
             constexpr int kk = decltype(kc)::value;
-            if constexpr (kk % 2 == 0) stage(f0, cur, kk + 1, f1, nullptr, 0, T_{}, F_{});
-            else stage(f1, cur, kk + 1, f0, nullptr, 0, T_{}, F_{});
+            if constexpr (kk % 2 == 0) stage(f0, cur, kk + 1, f1, nullptr, 0, T_{}, M0_{}, Z_{});
+            else stage(f1, cur, kk + 1, f0, nullptr, 0, T_{}, M0_{}, Z_{});
         });
     };
     if constexpr (S == 1) {
@@ -562,61 +628,61 @@ pipelined_gemm(KArgs args) {
             __syncthreads();
             load_frags(ring0, 0, f0);
             first_stages(ring0);
-            stage(f1, nullptr, 0, f0, nullptr, 0, F_{}, F_{});
+            stage(f1, nullptr, 0, f0, nullptr, 0, F_{}, M0_{}, Z_{});
             __syncthreads();
         }
     } else {
-        // prologue: k-tiles 0 .. S-1 fill every slot
-        static_for<0, S>([&](auto sc) {
-            if (sc.value < nk) issue(slot_of(sc), sc.value);
-        });
-        if (nk >= S) wait_vmcnt<(S - 1) * G::L>();
-        else wait_vmcnt<0>();
-        __syncthreads();
+        // The loop runs a whole number of S-groups: k-tiles t >= nk are copied as
+        // zeros (out-of-range offsets), so the extra MFMAs add exact zeros and the
+        // body needs no branches.
+        const int nt = ((nk + S - 1) / S) * S;
+        if constexpr (LDM == 0) {
+            // prologue: k-tiles 0 .. S-1 fill every slot; wait for k-tile 0
+            static_for<0, S>([&](auto sc) { issue(slot_of(sc), sc.value); });
+            wait_vmcnt<(S - 1) * G::L>();
+        } else {
+            // prologue: k-tiles 0 .. S-2 written, k-tile S-1 staged, its first CPS ops
+            // written and k-tile S loaded in their place (the window before k-tile 0)
+            static_for<0, S - 1>([&](auto sc) {
+                static_for<0, G::L>([&](auto jc) { gload_op(sc.value, jc); });
+                static_for<0, G::L>([&](auto jc) { lwrite_op(slot_of(sc), jc); });
+            });
+            static_for<0, G::L>([&](auto jc) { gload_op(S - 1, jc); });
+            static_for<0, CPS>([&](auto jc) {
+                lwrite_op(slot_of(std::integral_constant<int, S - 1>{}), jc);
+                gload_op(S, jc);
+            });
+        }
+        lds_barrier();
         load_frags(ring0, 0, f0);
 
         constexpr int STEADY = (S - 2) * G::L;
-        // k-tile t (< nk) in slot s, steady state (t+S < nk): the k-tiles t+1 .. t+S-1
-        // are all in flight, exactly the copies of t+2 .. t+S-1 may stay outstanding,
-        // and slot s is refilled with k-tile t+S during the last stage.
-        auto ktile_full = [&](auto sc, int t) __attribute__((always_inline)) {
+        // k-tile t in slot s.  Direct copies: k-tiles t+1 .. t+S-1 are in flight;
+        // after the barrier slot s is refilled with k-tile t+S.  Register staging:
+        // the window from one barrier to the next writes k-tile t+S into the slot
+        // the first barrier released and loads k-tile t+S+1, CPS ops per stage.
+        auto ktile = [&](auto sc, int t) __attribute__((always_inline)) {
             constexpr int s = decltype(sc)::value;
             char* cur = slot_of(sc);
+            char* prev = slot_of(std::integral_constant<int, (s + S - 1) % S>{});
             const char* nxt = slot_of(std::integral_constant<int, (s + 1) % S>{});
-            first_stages(cur);
-            wait_vmcnt<STEADY>();
-            __syncthreads();
-            stage(f1, nxt, 0, f0, cur, t + S, T_{}, T_{});
+            static_for<0, KSTEPS - 1>([&](auto kc) {
+                constexpr int kk = decltype(kc)::value;
+                using J = std::integral_constant<int, (kk + 1) * CPS>;
+                using MD = std::integral_constant<int, LDM == 1 ? 2 : 0>;
+                if constexpr (kk % 2 == 0) stage(f0, cur, kk + 1, f1, prev, t + S, T_{}, MD{}, J{});
+                else stage(f1, cur, kk + 1, f0, prev, t + S, T_{}, MD{}, J{});
+            });
+            if constexpr (LDM == 0) wait_vmcnt<STEADY>();
+            // every wave has finished reading slot s (released) and the next k-tile is
+            // complete in its slot
+            lds_barrier();
+            if constexpr (LDM == 0) stage(f1, nxt, 0, f0, cur, t + S, T_{}, M1_{}, Z_{});
+            else stage(f1, nxt, 0, f0, cur, t + S + 1, T_{}, M2_{}, Z_{});
         };
-        // k-tile t (< nk) near the end: the same decisions taken at run time.  Only the
-        // boundary (wait, barrier, refill, next reads) is conditional, never the MFMAs.
-        auto ktile_tail = [&](auto sc, int t) __attribute__((always_inline)) {
-            constexpr int s = decltype(sc)::value;
-            char* cur = slot_of(sc);
-            const char* nxt = slot_of(std::integral_constant<int, (s + 1) % S>{});
-            first_stages(cur);
-            if (t + 1 < nk) {
-                if (t + S < nk) wait_vmcnt<STEADY>();
-                else wait_vmcnt<0>();
-                __syncthreads();
-                if (t + S < nk) issue(cur, t + S);
-                load_frags(nxt, 0, f0);
-            }
-            fence();
-            mma(f1);
-            fence();
-        };
-        // steady state: S k-tiles per iteration, static slots, no branches
-        int t0 = 0;
-        for (; t0 + 2 * S <= nk; t0 += S) {
-            static_for<0, S>([&](auto sc) { ktile_full(sc, t0 + decltype(sc)::value); });
+        for (int t0 = 0; t0 < nt; t0 += S) {
+            static_for<0, S>([&](auto sc) { ktile(sc, t0 + decltype(sc)::value); });
         }
-        // drain: fewer than 2S k-tiles remain; t0 is a multiple of S
-        static_for<0, 2 * S - 1>([&](auto sc) {
-            constexpr int i = decltype(sc)::value;
-            const int t = t0 + i;
-            if (t < nk) ktile_tail(std::integral_constant<int, i % S>{}, t);
-        });
     }
 
     // ---- epilogue ------------------------------------------------------------
