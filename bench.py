@@ -127,7 +127,8 @@ def measured_traffic(workload: str, forced: bool):
 
 
 def parse_tile(spec):
-    """'256x256x64:2[:swizzle[:group_m[:staging]]]' -> the matching compiled configuration."""
+    """'256x256x64:2[:swizzle[:group_m[:staging[:WMxWN]]]]' -> the matching compiled
+    configuration (the first one in the table when the wave tile is not given)."""
     import software_pipelined_tiled_gemm_amd as spg
 
     parts = spec.split(":")
@@ -138,8 +139,11 @@ def parse_tile(spec):
     swz = int(parts[2]) if len(parts) > 2 else 1
     gm = int(parts[3]) if len(parts) > 3 else 0
     stg = int(parts[4]) if len(parts) > 4 else 0
+    wave = tuple(int(x) for x in parts[5].lower().split("x")) if len(parts) > 5 else None
     for i in range(spg.gemm_num_configs()):
         c = spg.gemm_list_config(i)
+        if wave is not None and (c.wave_m, c.wave_n) != wave:
+            continue
         if (c.block_m, c.block_n, c.block_k, c.stages, c.swizzle, c.staging) == (bm, bn, bk, st, swz, stg):
             if gm:
                 c.group_m = gm
@@ -156,7 +160,7 @@ def main():
     ap.add_argument("--workload", default="nn_bf16_8192",
                     help="workload name from workloads.WORKLOADS")
     ap.add_argument("--tile", default=None,
-                    help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging]]] "
+                    help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging[:WMxWN]]]] "
                          "(default: the library's choice)")
     ap.add_argument("--no-extra", action="store_true", help="skip the fp16 8192^3 extra line")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -113,10 +113,11 @@ bool pipelined_fits(int64_t M, int64_t N, int64_t K, gemm_b_layout bl) {
     return true;
 }
 
-const Variant* find_cfg(int bm, int bn, int bk, int stages, int staging) {
+const Variant* find_cfg(int bm, int bn, int bk, int stages, int staging, int wm, int wn) {
     for (const Variant& v : kVariants)
         if (v.cfg.block_m == bm && v.cfg.block_n == bn && v.cfg.block_k == bk &&
-            v.cfg.stages == stages && v.cfg.staging == staging && v.cfg.swizzle == 1)
+            v.cfg.stages == stages && v.cfg.staging == staging && v.cfg.swizzle == 1 &&
+            v.cfg.wave_m == wm && v.cfg.wave_n == wn)
             return &v;
     return nullptr;
 }
@@ -127,8 +128,9 @@ gemm_tile_config heuristic(int64_t M, int64_t N) {
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     const int64_t cus = 256;
     gemm_tile_config c;
-    if (tiles(256, 256) >= cus) c = find_cfg(256, 256, 64, 2, 0)->cfg;
-    else c = find_cfg(128, 128, 64, 3, 0)->cfg;
+    // 256x256 tiles with 8 waves (two per SIMD, 128x64 each) measured best at 8192^3
+    if (tiles(256, 256) >= cus) c = find_cfg(256, 256, 64, 2, 0, 128, 64)->cfg;
+    else c = find_cfg(128, 128, 64, 3, 0, 64, 64)->cfg;
     c.group_m = 8;
     c.xcd_remap = 1;
     return c;

@@ -116,7 +116,8 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ void dma16(const i32x4& rsrc, char* lds_dst, uint32_t voff) {
     const uint32_t m0 =
         __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(SPG_LDS char*)lds_dst);
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    // s_nop: one wait state between the M0 write and the LDS-DMA load that reads it
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(m0), "v"(voff), "s"(rsrc)
                  : "memory", "m0");
@@ -559,6 +560,10 @@ pipelined_gemm(KArgs args) {
     // hands the matrix pipe a new MFMA every step while the LDS and the copies are
     // fed in its shadow instead of in bursts.
     constexpr int NMMA = TN * TM;
+#ifndef SPG_READS_PER_STEP
+#define SPG_READS_PER_STEP 2
+#endif
+    constexpr int RPS = SPG_READS_PER_STEP;  // LDS reads issued per MFMA step
     constexpr int CPS = G::L / KSTEPS;  // register-staged copy ops per MFMA stage
     static_assert(G::L % KSTEPS == 0, "copy ops must split evenly over the stages");
     // One MFMA stage with its memory traffic interleaved: step i issues MFMA i of
@@ -575,7 +580,10 @@ pipelined_gemm(KArgs args) {
         constexpr int MD = decltype(mode)::value;
         constexpr int J0 = decltype(j0c)::value;
         constexpr int NCP = MD == 1 ? G::L : (MD == 2 ? CPS : 0);
-        constexpr int STEPS = NMMA > NRD ? (NMMA > NCP ? NMMA : NCP) : (NRD > NCP ? NRD : NCP);
+        // LDS reads are front-loaded, RPS per step, so the last read of the stage has
+        // most of the stage to return before the next stage's first MFMA needs it
+        constexpr int NRS = (NRD + RPS - 1) / RPS;
+        constexpr int STEPS = NMMA > NRS ? (NMMA > NCP ? NMMA : NCP) : (NRS > NCP ? NRS : NCP);
         static_for<0, STEPS>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             if constexpr (i < NMMA) {
@@ -587,7 +595,12 @@ pipelined_gemm(KArgs args) {
                 lwrite_op(cslot, std::integral_constant<int, J0 + i>{});
                 gload_op(ckt, std::integral_constant<int, J0 + i>{});
             }
-            if constexpr (RD && i < NRD) read_op(rslot, rkk, nx, std::integral_constant<int, i>{});
+            if constexpr (RD) {
+                static_for<0, RPS>([&](auto rc) {
+                    constexpr int r = i * RPS + decltype(rc)::value;
+                    if constexpr (r < NRD) read_op(rslot, rkk, nx, std::integral_constant<int, r>{});
+                });
+            }
             fence();
         });
     };

@@ -16,4 +16,8 @@
 #define SPG_V_9(...) SPG_INSTANTIATE_ALL(__VA_ARGS__)
 #define SPG_V_10(...)
 #define SPG_V_11(...)
+#define SPG_V_12(...)
+#define SPG_V_13(...)
+#define SPG_V_14(...)
+#define SPG_V_15(...)
 #include "variants.inc"
