@@ -59,7 +59,7 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1 } gemm_epilogue;
 
 /* Tile configuration of the pipelined kernel.
  *   block_m x block_n   output tile of one workgroup (128 or 256 each)
- *   block_k             K extent of one pipeline stage (64)
+ *   block_k             K extent of one pipeline stage (32 or 64)
  *   stages              LDS ring depth S (1 = no overlap, the serial K loop of the
  *                       TileLang tutorial's matmul_plain; 2..4 = loads of k-tile t+S-1
  *                       in flight while k-tile t is multiplied)
@@ -68,8 +68,10 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1 } gemm_epilogue;
  *   group_m             tile-raster group height in tiles (L2 reuse); 0 = default
  *   xcd_remap           1 = give each of the 8 XCDs a contiguous range of tiles
  *   staging             0 = k-tiles are copied straight from memory into LDS
- *                       (buffer_load ... lds); 1 = copied into VGPRs one k-tile ahead
- *                       and written to LDS with ds_write_b128
+ *                       (buffer_load ... lds), a k-tile's copies issued together;
+ *                       1 = copied into VGPRs one k-tile ahead and written to LDS
+ *                       with ds_write_b128; 2 = straight into LDS, the copies of a
+ *                       k-tile spread evenly between two barriers (stages >= 3)
  * The LDS a configuration needs is stages * (block_m + block_n) * block_k * 2 bytes
  * (the shared-memory bound of the TileLang tutorial's shared_bytes()), at most 160 KiB. */
 typedef struct {

@@ -24,6 +24,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "out of memory",
 DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
 B_LAYOUTS = {"kn": 0, "nk": 1}
 EPILOGUES = {"none": 0, "gelu_tanh": 1}
+STAGING = {0: "direct", 1: "vgpr", 2: "direct-spread"}
 
 
 class GemmError(RuntimeError):
@@ -54,7 +55,7 @@ class TileConfig(ctypes.Structure):
         return (f"TileConfig({d['block_m']}x{d['block_n']}x{d['block_k']}, S={d['stages']}, "
                 f"wave {d['wave_m']}x{d['wave_n']}, swizzle={d['swizzle']}, "
                 f"group_m={d['group_m']}, xcd_remap={d['xcd_remap']}, "
-                f"staging={'vgpr' if d['staging'] else 'direct'})")
+                f"staging={STAGING.get(d['staging'], d['staging'])})")
 
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_get_config", "gemm_autotune",

@@ -113,9 +113,8 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 // writes, and would otherwise wait for every outstanding copy before any LDS
 // read, serializing the ring.  The kernel orders these copies itself with
 // s_waitcnt vmcnt(N) and the per-k-tile barrier.
-__device__ __forceinline__ void dma16(const i32x4& rsrc, char* lds_dst, uint32_t voff) {
-    const uint32_t m0 =
-        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(SPG_LDS char*)lds_dst);
+__device__ __forceinline__ void dma16(const i32x4& rsrc, SPG_LDS char* lds_dst, uint32_t voff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
     // s_nop: one wait state between the M0 write and the LDS-DMA load that reads it
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
@@ -320,14 +319,20 @@ __device__ __forceinline__ int kswz_t(int r) {
 }
 
 // LDM selects how a k-tile reaches its LDS slot:
-//   0  direct-to-LDS copies (buffer_load ... lds), no VGPR staging;
+//   0  direct-to-LDS copies (buffer_load ... lds), no VGPR staging, all copies of
+//      k-tile t+S issued in the stage right after the barrier that frees slot t;
 //   1  register-staged: buffer_load_dwordx4 into VGPRs one k-tile ahead, then
 //      ds_write_b128 into the same swizzled slot layout.  LDS writes from VGPRs
 //      leave the LDS more read bandwidth than direct copies do.
+//   2  direct-to-LDS copies spread evenly over the whole window from one barrier
+//      to the next (L / KSTEPS per stage), so the vector-memory queue never
+//      backs up into the MFMA issue of a wave that is alone on its SIMD.  The
+//      last copies of a window land one k-tile before they are read, hence S >= 3.
 template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ, int LDM>
 __global__ void __launch_bounds__((Geom<BM, BN, BK, WM, WN, S>::NT))
 pipelined_gemm(KArgs args) {
     using G = Geom<BM, BN, BK, WM, WN, S>;
+    static_assert(LDM != 2 || S >= 3, "spread copies need a slot of slack");
     constexpr int TM = G::TM, TN = G::TN, A_BYTES = G::A_BYTES, KSTEPS = G::KSTEPS;
     constexpr int ROWB = G::ROWB;
     constexpr int A_DMA = G::A_DMA, B_DMA = G::B_DMA;
@@ -342,19 +347,20 @@ pipelined_gemm(KArgs args) {
     __shared__ __attribute__((aligned(1024))) char ring5[S > 5 ? G::STAGE : 16];
 
     // ring slot s as a compile-time choice of array (see the header comment)
-    auto slot_of = [&](auto sc) -> char* {
+    auto slot_of = [&](auto sc) -> SPG_LDS char* {
         constexpr int v = decltype(sc)::value;
-        if constexpr (v == 0) return ring0;
-        else if constexpr (v == 1) return ring1;
-        else if constexpr (v == 2) return ring2;
-        else if constexpr (v == 3) return ring3;
-        else if constexpr (v == 4) return ring4;
-        else return ring5;
+        if constexpr (v == 0) return (SPG_LDS char*)ring0;
+        else if constexpr (v == 1) return (SPG_LDS char*)ring1;
+        else if constexpr (v == 2) return (SPG_LDS char*)ring2;
+        else if constexpr (v == 3) return (SPG_LDS char*)ring3;
+        else if constexpr (v == 4) return (SPG_LDS char*)ring4;
+        else return (SPG_LDS char*)ring5;
     };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // the wave index is uniform: kept in an SGPR, so are the copy addresses derived from it
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / G::WAVES_N;
     const int wn = wave % G::WAVES_N;
 
@@ -363,33 +369,66 @@ pipelined_gemm(KArgs args) {
     const int M = args.M, N = args.N, K = args.K;
     const int m0 = tm * BM, n0 = tn * BN;
     const int nk = (K + BK - 1) / BK;
+    // k-tile kt covers k in [kt*BK - pad, kt*BK - pad + BK) with pad = (-K) mod BK:
+    // the partial k-tile, when K % BK != 0, is the first one and its k < 0 part
+    // reads as zeros.  Every later k-tile lies inside [0, K), so only the copies
+    // of k-tile 0 (all issued before the K loop) carry per-lane masks.  pad is a
+    // multiple of 8 (K % 8 == 0), i.e. of the 16-byte copy granule.
+    const int pad = (BK - K % BK) % BK;
 
-    // ---- buffer resources: bytes past the end read as zero -------------------
+    // ---- copy sources: one buffer resource per operand and k-tile -------------
+    // The resource of k-tile kt starts at the tile's first k and ends where this
+    // workgroup's rows of the operand end, so rows past M (A) or past N (B stored
+    // [N,K]) read as zero; past the last k-tile it is empty and reads zero.  The
+    // per-lane offsets inside it are the same for every k-tile, so a copy is one
+    // M0 write and one buffer_load; the per-k-tile work is scalar.
     const int a_rows = (M - m0) < BM ? (M - m0) : BM;
-    const void* a_base = args.A + (size_t)m0 * K;
+    const uint64_t a_base = (uint64_t)(uintptr_t)(args.A + (size_t)m0 * K);
     const uint32_t a_bytes = (uint32_t)a_rows * (uint32_t)K * 2u;
-    const void* b_base;
-    uint32_t b_bytes;
+    uint64_t b_base;
+    uint32_t b_bytes, b_kb;  // b_kb: bytes between consecutive k
     if constexpr (B_NK) {
         const int b_rows = (N - n0) < BN ? (N - n0) : BN;
-        b_base = args.B + (size_t)n0 * K;
+        b_base = (uint64_t)(uintptr_t)(args.B + (size_t)n0 * K);
         b_bytes = (uint32_t)b_rows * (uint32_t)K * 2u;
+        b_kb = 2u;
     } else {
-        // rows k >= K fall past num_records; columns past N are masked per lane
-        b_base = args.B + n0;
+        b_base = (uint64_t)(uintptr_t)(args.B + n0);
         b_bytes = (uint32_t)(((size_t)K * N - n0) * 2u);
+        b_kb = 2u * (uint32_t)N;
     }
-    const i32x4 rA = make_rsrc(a_base, a_bytes);
-    const i32x4 rB = make_rsrc(b_base, b_bytes);
-    const __amdgpu_buffer_rsrc_t rAb = make_rsrc_b(a_base, a_bytes);
-    const __amdgpu_buffer_rsrc_t rBb = make_rsrc_b(b_base, b_bytes);
+    // start address and size of an operand's resource for k-tile kt
+    auto window = [&](uint64_t base, uint32_t bytes, uint32_t kb, int kt, uint64_t& p,
+                      uint32_t& nr) __attribute__((always_inline)) {
+        const int64_t shift = (int64_t)(kt * BK - pad) * (int64_t)kb;  // < 0 only for kt = 0
+        p = base + (uint64_t)shift;
+        nr = kt < nk ? bytes - (uint32_t)shift : 0u;
+    };
+    struct DmaSrc { i32x4 a, b; };
+    auto dma_src = [&](int kt) __attribute__((always_inline)) -> DmaSrc {
+        uint64_t pa, pb;
+        uint32_t na, nb;
+        window(a_base, a_bytes, 2u, kt, pa, na);
+        window(b_base, b_bytes, b_kb, kt, pb, nb);
+        return DmaSrc{make_rsrc((const void*)(uintptr_t)pa, na), make_rsrc((const void*)(uintptr_t)pb, nb)};
+    };
+    struct RegSrc { __amdgpu_buffer_rsrc_t a, b; };
+    auto reg_src = [&](int kt) __attribute__((always_inline)) -> RegSrc {
+        uint64_t pa, pb;
+        uint32_t na, nb;
+        window(a_base, a_bytes, 2u, kt, pa, na);
+        window(b_base, b_bytes, b_kb, kt, pb, nb);
+        return RegSrc{make_rsrc_b((const void*)(uintptr_t)pa, na), make_rsrc_b((const void*)(uintptr_t)pb, nb)};
+    };
 
-    // ---- per-lane DMA source offsets (k-tile 0) ------------------------------
-    // DMA instruction d of the tile writes LDS bytes [d*1024, d*1024+1024): lane i
+    // ---- per-lane copy offsets -----------------------------------------------
+    // Copy instruction d of a k-tile writes LDS bytes [d*1024, d*1024+1024): lane i
     // lands at byte i*16, i.e. row d*RPI + i/CPR, physical chunk i%CPR; it fetches
-    // the logical chunk that the swizzle puts there.
+    // the logical chunk that the swizzle puts there.  kinA/kinB: the k offset of the
+    // lane's 8 elements inside the k-tile, for the masks of k-tile 0.  Columns past
+    // N of a [K,N] B point past every resource and read as zero.
     uint32_t offA[A_DMA];
-    int colA[A_DMA];
+    int kinA[A_DMA];
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
         const int d = wave * A_DMA + j;
@@ -397,10 +436,10 @@ pipelined_gemm(KArgs args) {
         const int p = lane % CPR_K;
         const int c = SWZ ? (p ^ kswz_t<BK>(r)) : p;
         offA[j] = (uint32_t)r * (uint32_t)K * 2u + (uint32_t)c * 16u;
-        colA[j] = c * 8;
+        kinA[j] = c * 8;
     }
     uint32_t offB[B_DMA];
-    int colB[B_DMA];
+    int kinB[B_DMA];
 #pragma unroll
     for (int j = 0; j < B_DMA; ++j) {
         const int d = wave * B_DMA + j;
@@ -409,65 +448,59 @@ pipelined_gemm(KArgs args) {
             const int p = lane % CPR_K;
             const int c = SWZ ? (p ^ kswz_t<BK>(r)) : p;
             offB[j] = (uint32_t)r * (uint32_t)K * 2u + (uint32_t)c * 16u;
-            colB[j] = c * 8;
+            kinB[j] = c * 8;
         } else {
             constexpr int CPR = BN / 8;          // 16-B chunks per [K,N] row
             constexpr int RP = 64 / CPR;         // rows per wave instruction
             const int r = d * RP + lane / CPR;
             const int p = lane % CPR;
             const int c = SWZ ? (p ^ nswz(r)) : p;
-            offB[j] = (uint32_t)r * (uint32_t)N * 2u + (uint32_t)c * 16u;
-            colB[j] = c * 8;
+            offB[j] = n0 + c * 8 + 8 > N ? kOOB : (uint32_t)r * (uint32_t)N * 2u + (uint32_t)c * 16u;
+            kinB[j] = r;
         }
     }
-    const bool k_tail = (K % BK) != 0;
-    const bool n_tail = !B_NK && (n0 + BN > N);
 
-    // Copy op j (compile-time) of k-tile kt: j < A_DMA moves A rows, the rest B.
-    // Each moves 16 B per lane into LDS bytes lds_off(j) + 16*lane of the slot.
-    // On the last k-tile, chunks past K (or columns past N for a [K,N] B) are
-    // redirected past the buffer end and read as zero.
-    auto src_off = [&](int kt, auto jc) __attribute__((always_inline)) -> uint32_t {
+    // Offset of copy op j (compile-time): j < A_DMA moves A rows, the rest B.  On
+    // k-tile 0 (FIRST) the lanes whose elements lie at k < 0 read zero.
+    auto src_off = [&](auto jc, auto first) __attribute__((always_inline)) -> uint32_t {
         constexpr int j = decltype(jc)::value;
-        const int k0 = kt * BK;
-        uint32_t off;
+        constexpr bool FIRST = decltype(first)::value;
         if constexpr (j < A_DMA) {
-            off = offA[j] + (uint32_t)k0 * 2u;
-            if (k_tail && kt == nk - 1 && k0 + colA[j] + 8 > K) off = kOOB;
+            if constexpr (FIRST) return kinA[j] < pad ? kOOB : offA[j];
+            else return offA[j];
         } else {
             constexpr int jb = j - A_DMA;
-            if constexpr (B_NK) {
-                off = offB[jb] + (uint32_t)k0 * 2u;
-                if (k_tail && kt == nk - 1 && k0 + colB[jb] + 8 > K) off = kOOB;
-            } else {
-                off = offB[jb] + (uint32_t)k0 * (uint32_t)N * 2u;
-                if (n_tail && n0 + colB[jb] + 8 > N) off = kOOB;
-            }
+            if constexpr (FIRST) return kinB[jb] < pad ? kOOB : offB[jb];
+            else return offB[jb];
         }
-        return kt < nk ? off : kOOB;  // past the last k-tile: zeros
     };
+    // op j writes LDS bytes lds_off(j) + 16*lane of the slot
     auto lds_off = [&](auto jc) __attribute__((always_inline)) -> int {
         constexpr int j = decltype(jc)::value;
         if constexpr (j < A_DMA) return (wave * A_DMA + j) * 1024;
         else return A_BYTES + (wave * B_DMA + (j - A_DMA)) * 1024;
     };
-    auto dma_op = [&](char* slot, int kt, auto jc) __attribute__((always_inline)) {
+    using NotFirst = std::false_type;
+    using First = std::true_type;
+    auto dma_op = [&](SPG_LDS char* slot, const DmaSrc& src, auto jc, auto first)
+                      __attribute__((always_inline)) {
         constexpr int j = decltype(jc)::value;
-        dma16(j < A_DMA ? rA : rB, slot + lds_off(jc), src_off(kt, jc));
+        dma16(j < A_DMA ? src.a : src.b, slot + lds_off(jc), src_off(jc, first));
     };
     // register staging (LDM 1): one k-tile of copies in flight in VGPRs
     u32x4 stage_regs[G::L];
-    auto gload_op = [&](int kt, auto jc) __attribute__((always_inline)) {
+    auto gload_op = [&](const RegSrc& src, auto jc, auto first) __attribute__((always_inline)) {
         constexpr int j = decltype(jc)::value;
-        stage_regs[j] = __builtin_amdgcn_raw_buffer_load_b128(j < A_DMA ? rAb : rBb,
-                                                        (int)src_off(kt, jc), 0, 0);
+        stage_regs[j] = __builtin_amdgcn_raw_buffer_load_b128(j < A_DMA ? src.a : src.b,
+                                                              (int)src_off(jc, first), 0, 0);
     };
-    auto lwrite_op = [&](char* slot, auto jc) __attribute__((always_inline)) {
+    auto lwrite_op = [&](SPG_LDS char* slot, auto jc) __attribute__((always_inline)) {
         constexpr int j = decltype(jc)::value;
         *(SPG_LDS u32x4*)(slot + lds_off(jc) + lane * 16) = stage_regs[j];
     };
-    auto issue = [&](char* slot, int kt) __attribute__((always_inline)) {
-        static_for<0, G::L>([&](auto jc) { dma_op(slot, kt, jc); });
+    auto issue = [&](SPG_LDS char* slot, int kt, auto first) __attribute__((always_inline)) {
+        const DmaSrc src = dma_src(kt);
+        static_for<0, G::L>([&](auto jc) { dma_op(slot, src, jc, first); });
     };
 
     // ---- per-lane LDS read offsets -------------------------------------------
@@ -523,7 +556,7 @@ pipelined_gemm(KArgs args) {
     // the B columns (one ds_read_b128 each for [N,K] storage, two transposing
     // reads -- k 0..3 and 4..7 of the lane's 8 -- for [K,N] storage).
     constexpr int NRD = TM + (B_NK ? TN : 2 * TN);
-    auto read_op = [&](const char* slot, int kk, Frags& f, auto rc) __attribute__((always_inline)) {
+    auto read_op = [&](const SPG_LDS char* slot, int kk, Frags& f, auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
         if constexpr (r < TM) {
             f.a[r] = *(const SPG_LDS u32x4*)(slot + aoff[kk] + r * 32 * ROWB);
@@ -540,7 +573,7 @@ pipelined_gemm(KArgs args) {
             f.b[bn][2 * h + 1] = v2[1];
         }
     };
-    auto load_frags = [&](const char* slot, int kk, Frags& f) __attribute__((always_inline)) {
+    auto load_frags = [&](const SPG_LDS char* slot, int kk, Frags& f) __attribute__((always_inline)) {
         static_for<0, NRD>([&](auto rc) { read_op(slot, kk, f, rc); });
     };
     auto mma = [&](const Frags& f) __attribute__((always_inline)) {
@@ -553,33 +586,29 @@ pipelined_gemm(KArgs args) {
     // keep each stage's loads and MFMAs together: no motion across stage boundaries
     auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
 
-    // One MFMA stage with its memory traffic interleaved: step i issues MFMA i of
-    // `now`, then LDS read i of the next stage (into `nx`, from `rslot` at k-step
-    // rkk) and, when `dslot` is given, DMA op i of k-tile `dkt`.  A scheduling
-    // barrier after every step keeps this order, so the single wave of each SIMD
-    // hands the matrix pipe a new MFMA every step while the LDS and the copies are
-    // fed in its shadow instead of in bursts.
     constexpr int NMMA = TN * TM;
 #ifndef SPG_READS_PER_STEP
 #define SPG_READS_PER_STEP 2
 #endif
     constexpr int RPS = SPG_READS_PER_STEP;  // LDS reads issued per MFMA step
-    constexpr int CPS = G::L / KSTEPS;  // register-staged copy ops per MFMA stage
+    constexpr int CPS = G::L / KSTEPS;       // copy ops per stage when spread over a window
     static_assert(G::L % KSTEPS == 0, "copy ops must split evenly over the stages");
     // One MFMA stage with its memory traffic interleaved: step i issues MFMA i of
-    // `now`, then LDS read i of the next stage (into `nx`, from `rslot` at k-step
-    // rkk) and copy op i.  MODE 1: direct-to-LDS copy op i of k-tile ckt into
-    // cslot; MODE 2: copy ops J0.. J0+CPS-1 of the register-staged pipeline (write
-    // the staged data into cslot, then load k-tile ckt into the freed registers).
-    // A scheduling barrier after every step keeps this order, so the single wave
-    // of each SIMD hands the matrix pipe a new MFMA every step while the LDS and
-    // the copies are fed in its shadow instead of in bursts.
-    auto stage = [&](const Frags& now, const char* rslot, int rkk, Frags& nx, char* cslot,
-                     int ckt, auto do_read, auto mode, auto j0c) __attribute__((always_inline)) {
+    // `now`, then copy op i and RPS LDS reads of the next stage (into `nx`, from
+    // `rslot` at k-step rkk).  Copy modes: 1, all L direct-to-LDS ops of the k-tile
+    // whose resources are `src`, into `cslot`; 2, register-staged ops J0 .. J0+CPS-1
+    // (write the staged data into cslot, then load the k-tile of `src` into the
+    // freed registers); 3, direct-to-LDS ops J0 .. J0+CPS-1.  A scheduling barrier
+    // after every step keeps this order, so each wave hands the matrix pipe a new
+    // MFMA every step while the LDS and the copies are fed in its shadow instead of
+    // in bursts.
+    auto stage = [&](const Frags& now, const SPG_LDS char* rslot, int rkk, Frags& nx,
+                     SPG_LDS char* cslot, const auto& src, auto do_read, auto mode, auto j0c)
+                     __attribute__((always_inline)) {
         constexpr bool RD = decltype(do_read)::value;
         constexpr int MD = decltype(mode)::value;
         constexpr int J0 = decltype(j0c)::value;
-        constexpr int NCP = MD == 1 ? G::L : (MD == 2 ? CPS : 0);
+        constexpr int NCP = MD == 1 ? G::L : (MD >= 2 ? CPS : 0);
         // LDS reads are front-loaded, RPS per step, so the last read of the stage has
         // most of the stage to return before the next stage's first MFMA needs it
         constexpr int NRS = (NRD + RPS - 1) / RPS;
@@ -590,11 +619,14 @@ pipelined_gemm(KArgs args) {
                 constexpr int bn = i / TM, bm = i % TM;
                 acc[bn][bm] = mfma<BF16>(now.b[bn], now.a[bm], acc[bn][bm]);
             }
-            if constexpr (MD == 1 && i < NCP) dma_op(cslot, ckt, std::integral_constant<int, i>{});
+            if constexpr (MD == 1 && i < NCP)
+                dma_op(cslot, src, std::integral_constant<int, i>{}, NotFirst{});
             if constexpr (MD == 2 && i < NCP) {
                 lwrite_op(cslot, std::integral_constant<int, J0 + i>{});
-                gload_op(ckt, std::integral_constant<int, J0 + i>{});
+                gload_op(src, std::integral_constant<int, J0 + i>{}, NotFirst{});
             }
+            if constexpr (MD == 3 && i < NCP)
+                dma_op(cslot, src, std::integral_constant<int, J0 + i>{}, NotFirst{});
             if constexpr (RD) {
                 static_for<0, RPS>([&](auto rc) {
                     constexpr int r = i * RPS + decltype(rc)::value;
@@ -609,7 +641,9 @@ pipelined_gemm(KArgs args) {
     using M0_ = std::integral_constant<int, 0>;
     using M1_ = std::integral_constant<int, 1>;
     using M2_ = std::integral_constant<int, 2>;
+    using M3_ = std::integral_constant<int, 3>;
     using Z_ = std::integral_constant<int, 0>;
+    constexpr int kNoCopy = 0;
 
     Frags f0, f1;
 
@@ -618,7 +652,7 @@ pipelined_gemm(KArgs args) {
     // One k-tile = KSTEPS MFMA stages of 16 k.  Stage kk reads the fragments of
     // stage kk+1 while the MFMAs of stage kk run.  Before the last stage -- after
     // this wave's last LDS read of the current slot -- sits the one barrier of the
-    // k-tile: once every wave has passed it, (a) the next k-tile, whose DMA this
+    // k-tile: once every wave has passed it, (a) the next k-tile, whose copies this
     // wave has waited for, is visible to all, and (b) nobody reads the current slot
     // any more, so it is released and refilled with k-tile t+S while the MFMAs of
     // the last stage (which read registers, not LDS) still run.  The last stage
@@ -626,72 +660,100 @@ pipelined_gemm(KArgs args) {
     // work across the k-tile boundary.  KSTEPS is even, so stage kk computes from
     // f0 when kk is even and the last stage from f1.
     static_assert(KSTEPS % 2 == 0, "fragment double buffer assumes an even k-step count");
-    auto first_stages = [&](const char* cur) __attribute__((always_inline)) {
+    auto first_stages = [&](const SPG_LDS char* cur) __attribute__((always_inline)) {
         static_for<0, KSTEPS - 1>([&](auto kc) {
             constexpr int kk = decltype(kc)::value;
-            if constexpr (kk % 2 == 0) stage(f0, cur, kk + 1, f1, nullptr, 0, T_{}, M0_{}, Z_{});
-            else stage(f1, cur, kk + 1, f0, nullptr, 0, T_{}, M0_{}, Z_{});
+            if constexpr (kk % 2 == 0) stage(f0, cur, kk + 1, f1, nullptr, kNoCopy, T_{}, M0_{}, Z_{});
+            else stage(f1, cur, kk + 1, f0, nullptr, kNoCopy, T_{}, M0_{}, Z_{});
         });
     };
     if constexpr (S == 1) {
         // the serial K loop: copy, wait, multiply, and only then let the next copy in
+        SPG_LDS char* r0 = slot_of(Z_{});
+        issue(r0, 0, First{});
         for (int t = 0; t < nk; ++t) {
-            issue(ring0, t);
             wait_vmcnt<0>();
             __syncthreads();
-            load_frags(ring0, 0, f0);
-            first_stages(ring0);
-            stage(f1, nullptr, 0, f0, nullptr, 0, F_{}, M0_{}, Z_{});
+            load_frags(r0, 0, f0);
+            first_stages(r0);
+            stage(f1, nullptr, 0, f0, nullptr, kNoCopy, F_{}, M0_{}, Z_{});
             __syncthreads();
+            issue(r0, t + 1, NotFirst{});  // past the last k-tile: zeros
         }
     } else {
         // The loop runs a whole number of S-groups: k-tiles t >= nk are copied as
-        // zeros (out-of-range offsets), so the extra MFMAs add exact zeros and the
-        // body needs no branches.
+        // zeros (empty resources), so the extra MFMAs add exact zeros and the body
+        // needs no branches.
         const int nt = ((nk + S - 1) / S) * S;
+        auto first_of = [](auto sc) { return std::integral_constant<bool, decltype(sc)::value == 0>{}; };
         if constexpr (LDM == 0) {
             // prologue: k-tiles 0 .. S-1 fill every slot; wait for k-tile 0
-            static_for<0, S>([&](auto sc) { issue(slot_of(sc), sc.value); });
+            static_for<0, S>([&](auto sc) { issue(slot_of(sc), sc.value, first_of(sc)); });
             wait_vmcnt<(S - 1) * G::L>();
+        } else if constexpr (LDM == 2) {
+            // prologue: k-tiles 0 .. S-2 whole, and the first CPS copies of k-tile S-1
+            // (those the window before k-tile 0 would have issued); wait for k-tile 0
+            static_for<0, S - 1>([&](auto sc) { issue(slot_of(sc), sc.value, first_of(sc)); });
+            const DmaSrc src = dma_src(S - 1);
+            static_for<0, CPS>([&](auto jc) {
+                dma_op(slot_of(std::integral_constant<int, S - 1>{}), src, jc, NotFirst{});
+            });
+            wait_vmcnt<(S - 2) * G::L + CPS>();
         } else {
             // prologue: k-tiles 0 .. S-2 written, k-tile S-1 staged, its first CPS ops
             // written and k-tile S loaded in their place (the window before k-tile 0)
             static_for<0, S - 1>([&](auto sc) {
-                static_for<0, G::L>([&](auto jc) { gload_op(sc.value, jc); });
+                const RegSrc src = reg_src(sc.value);
+                static_for<0, G::L>([&](auto jc) { gload_op(src, jc, first_of(sc)); });
                 static_for<0, G::L>([&](auto jc) { lwrite_op(slot_of(sc), jc); });
             });
-            static_for<0, G::L>([&](auto jc) { gload_op(S - 1, jc); });
+            const RegSrc src1 = reg_src(S - 1), src2 = reg_src(S);
+            static_for<0, G::L>([&](auto jc) { gload_op(src1, jc, NotFirst{}); });
             static_for<0, CPS>([&](auto jc) {
                 lwrite_op(slot_of(std::integral_constant<int, S - 1>{}), jc);
-                gload_op(S, jc);
+                gload_op(src2, jc, NotFirst{});
             });
         }
         lds_barrier();
-        load_frags(ring0, 0, f0);
+        load_frags(slot_of(Z_{}), 0, f0);
 
         constexpr int STEADY = (S - 2) * G::L;
         // k-tile t in slot s.  Direct copies: k-tiles t+1 .. t+S-1 are in flight;
-        // after the barrier slot s is refilled with k-tile t+S.  Register staging:
-        // the window from one barrier to the next writes k-tile t+S into the slot
-        // the first barrier released and loads k-tile t+S+1, CPS ops per stage.
+        // after the barrier slot s is refilled with k-tile t+S (mode 0 all at once,
+        // mode 2 spread over the window up to the next barrier, which also moves
+        // the rest of k-tile t+S-1 into slot s-1).  Register staging: the window
+        // from one barrier to the next writes k-tile t+S into the slot the first
+        // barrier released and loads k-tile t+S+1, CPS ops per stage.
         auto ktile = [&](auto sc, int t) __attribute__((always_inline)) {
             constexpr int s = decltype(sc)::value;
-            char* cur = slot_of(sc);
-            char* prev = slot_of(std::integral_constant<int, (s + S - 1) % S>{});
-            const char* nxt = slot_of(std::integral_constant<int, (s + 1) % S>{});
-            static_for<0, KSTEPS - 1>([&](auto kc) {
-                constexpr int kk = decltype(kc)::value;
-                using J = std::integral_constant<int, (kk + 1) * CPS>;
-                using MD = std::integral_constant<int, LDM == 1 ? 2 : 0>;
-                if constexpr (kk % 2 == 0) stage(f0, cur, kk + 1, f1, prev, t + S, T_{}, MD{}, J{});
-                else stage(f1, cur, kk + 1, f0, prev, t + S, T_{}, MD{}, J{});
-            });
-            if constexpr (LDM == 0) wait_vmcnt<STEADY>();
+            SPG_LDS char* cur = slot_of(sc);
+            SPG_LDS char* prev = slot_of(std::integral_constant<int, (s + S - 1) % S>{});
+            const SPG_LDS char* nxt = slot_of(std::integral_constant<int, (s + 1) % S>{});
+            auto src_of = [&](int kt) __attribute__((always_inline)) {
+                if constexpr (LDM == 1) return reg_src(kt);
+                else return dma_src(kt);
+            };
+            {
+                // register staging writes k-tile t+S-1 into prev and loads k-tile t+S;
+                // spread copies move the rest of k-tile t+S-1 into prev
+                const auto src = src_of(LDM == 1 ? t + S : t + S - 1);
+                static_for<0, KSTEPS - 1>([&](auto kc) {
+                    constexpr int kk = decltype(kc)::value;
+                    using J = std::integral_constant<int, (kk + 1) * CPS>;
+                    using MD = std::integral_constant<int, LDM == 0 ? 0 : (LDM == 1 ? 2 : 3)>;
+                    if constexpr (kk % 2 == 0) stage(f0, cur, kk + 1, f1, prev, src, T_{}, MD{}, J{});
+                    else stage(f1, cur, kk + 1, f0, prev, src, T_{}, MD{}, J{});
+                });
+            }
+            if constexpr (LDM != 1) wait_vmcnt<STEADY>();
             // every wave has finished reading slot s (released) and the next k-tile is
             // complete in its slot
             lds_barrier();
-            if constexpr (LDM == 0) stage(f1, nxt, 0, f0, cur, t + S, T_{}, M1_{}, Z_{});
-            else stage(f1, nxt, 0, f0, cur, t + S + 1, T_{}, M2_{}, Z_{});
+            {
+                const auto src = src_of(LDM == 1 ? t + S + 1 : t + S);
+                using MD = std::integral_constant<int, LDM == 0 ? 1 : (LDM == 1 ? 2 : 3)>;
+                stage(f1, nxt, 0, f0, cur, src, T_{}, MD{}, Z_{});
+            }
         };
         for (int t0 = 0; t0 < nt; t0 += S) {
             static_for<0, S>([&](auto sc) { ktile(sc, t0 + decltype(sc)::value); });
@@ -699,6 +761,9 @@ pipelined_gemm(KArgs args) {
     }
 
     // ---- epilogue ------------------------------------------------------------
+    // the loop leaves zero-fill copies of k-tiles >= nt in flight: let them land
+    // before the ring is reused for staging
+    wait_vmcnt<0>();
     __syncthreads();  // the ring is drained and free for staging
     char* stg;
     {

@@ -20,4 +20,6 @@
 #define SPG_V_13(...)
 #define SPG_V_14(...) SPG_INSTANTIATE_ALL(__VA_ARGS__)
 #define SPG_V_15(...)
+#define SPG_V_16(...)
+#define SPG_V_17(...)
 #include "variants.inc"
