@@ -127,8 +127,8 @@ def measured_traffic(workload: str, forced: bool):
 
 
 def parse_tile(spec):
-    """'256x256x64:2[:swizzle[:group_m[:staging[:WMxWN]]]]' -> the matching compiled
-    configuration (the first one in the table when the wave tile is not given)."""
+    """'256x256x64:2[:swizzle[:group_m[:staging[:WMxWN[:lookahead]]]]]' -> the matching
+    compiled configuration (the first one in the table when the wave tile is not given)."""
     import software_pipelined_tiled_gemm_amd as spg
 
     parts = spec.split(":")
@@ -140,9 +140,12 @@ def parse_tile(spec):
     gm = int(parts[3]) if len(parts) > 3 else 0
     stg = int(parts[4]) if len(parts) > 4 else 0
     wave = tuple(int(x) for x in parts[5].lower().split("x")) if len(parts) > 5 else None
+    look = int(parts[6]) if len(parts) > 6 else 1
     for i in range(spg.gemm_num_configs()):
         c = spg.gemm_list_config(i)
         if wave is not None and (c.wave_m, c.wave_n) != wave:
+            continue
+        if c.lookahead != look:
             continue
         if (c.block_m, c.block_n, c.block_k, c.stages, c.swizzle, c.staging) == (bm, bn, bk, st, swz, stg):
             if gm:
@@ -160,7 +163,7 @@ def main():
     ap.add_argument("--workload", default="nn_bf16_8192",
                     help="workload name from workloads.WORKLOADS")
     ap.add_argument("--tile", default=None,
-                    help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging[:WMxWN]]]] "
+                    help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging[:WMxWN[:lookahead]]]]] "
                          "(default: the library's choice)")
     ap.add_argument("--no-extra", action="store_true", help="skip the fp16 8192^3 extra line")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -72,6 +72,9 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1 } gemm_epilogue;
  *                       1 = copied into VGPRs one k-tile ahead and written to LDS
  *                       with ds_write_b128; 2 = straight into LDS, the copies of a
  *                       k-tile spread evenly between two barriers (stages >= 3)
+ *   lookahead           MFMA k-steps between the LDS read of an operand fragment and
+ *                       its use: 1 (two fragment sets in registers) or 2 (four sets;
+ *                       block_k 64, stages >= 2)
  * The LDS a configuration needs is stages * (block_m + block_n) * block_k * 2 bytes
  * (the shared-memory bound of the TileLang tutorial's shared_bytes()), at most 160 KiB. */
 typedef struct {
@@ -82,6 +85,7 @@ typedef struct {
     int32_t group_m;
     int32_t xcd_remap;
     int32_t staging;
+    int32_t lookahead;
 } gemm_tile_config;
 
 typedef struct gemm_plan* gemm_handle;

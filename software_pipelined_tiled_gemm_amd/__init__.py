@@ -38,7 +38,12 @@ class TileConfig(ctypes.Structure):
                 ("block_k", ctypes.c_int32), ("stages", ctypes.c_int32),
                 ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32),
                 ("swizzle", ctypes.c_int32), ("group_m", ctypes.c_int32),
-                ("xcd_remap", ctypes.c_int32), ("staging", ctypes.c_int32)]
+                ("xcd_remap", ctypes.c_int32), ("staging", ctypes.c_int32),
+                ("lookahead", ctypes.c_int32)]
+
+    def __init__(self, **kw):
+        kw.setdefault("lookahead", 1)
+        super().__init__(**kw)
 
     def as_dict(self):
         return {k: int(getattr(self, k)) for k, _ in self._fields_}
@@ -47,7 +52,7 @@ class TileConfig(ctypes.Structure):
     def from_dict(cls, d):
         c = cls()
         for k, _ in cls._fields_:
-            setattr(c, k, int(d.get(k, 0)))
+            setattr(c, k, int(d.get(k, 1 if k == "lookahead" else 0)))
         return c
 
     def __repr__(self):
@@ -55,7 +60,7 @@ class TileConfig(ctypes.Structure):
         return (f"TileConfig({d['block_m']}x{d['block_n']}x{d['block_k']}, S={d['stages']}, "
                 f"wave {d['wave_m']}x{d['wave_n']}, swizzle={d['swizzle']}, "
                 f"group_m={d['group_m']}, xcd_remap={d['xcd_remap']}, "
-                f"staging={STAGING.get(d['staging'], d['staging'])})")
+                f"staging={STAGING.get(d['staging'], d['staging'])}, lookahead={d['lookahead']})")
 
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_get_config", "gemm_autotune",

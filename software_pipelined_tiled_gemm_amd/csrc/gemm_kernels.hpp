@@ -328,11 +328,19 @@ __device__ __forceinline__ int kswz_t(int r) {
 //      to the next (L / KSTEPS per stage), so the vector-memory queue never
 //      backs up into the MFMA issue of a wave that is alone on its SIMD.  The
 //      last copies of a window land one k-tile before they are read, hence S >= 3.
-template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ, int LDM>
+//
+// PF (lookahead) is the number of MFMA k-steps between the LDS read of an operand
+// fragment and its use: 1 keeps two fragment sets in registers, 2 keeps four and
+// gives every read a whole extra stage to return, which a wave alone on its SIMD
+// needs when the LDS is busy.  The barrier of a k-tile sits PF stages before its
+// end, right after the last read of the slot.
+template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ, int LDM,
+          int PF>
 __global__ void __launch_bounds__((Geom<BM, BN, BK, WM, WN, S>::NT))
 pipelined_gemm(KArgs args) {
     using G = Geom<BM, BN, BK, WM, WN, S>;
     static_assert(LDM != 2 || S >= 3, "spread copies need a slot of slack");
+    static_assert(PF == 1 || (PF == 2 && BK == 64 && S > 1), "lookahead 2 needs four k-steps per k-tile");
     constexpr int TM = G::TM, TN = G::TN, A_BYTES = G::A_BYTES, KSTEPS = G::KSTEPS;
     constexpr int ROWB = G::ROWB;
     constexpr int A_DMA = G::A_DMA, B_DMA = G::B_DMA;
@@ -608,7 +616,7 @@ pipelined_gemm(KArgs args) {
         constexpr bool RD = decltype(do_read)::value;
         constexpr int MD = decltype(mode)::value;
         constexpr int J0 = decltype(j0c)::value;
-        constexpr int NCP = MD == 1 ? G::L : (MD >= 2 ? CPS : 0);
+        constexpr int NCP = MD == 1 ? G::L / PF : (MD >= 2 ? CPS : 0);
         // LDS reads are front-loaded, RPS per step, so the last read of the stage has
         // most of the stage to return before the next stage's first MFMA needs it
         constexpr int NRS = (NRD + RPS - 1) / RPS;
@@ -620,7 +628,7 @@ pipelined_gemm(KArgs args) {
                 acc[bn][bm] = mfma<BF16>(now.b[bn], now.a[bm], acc[bn][bm]);
             }
             if constexpr (MD == 1 && i < NCP)
-                dma_op(cslot, src, std::integral_constant<int, i>{}, NotFirst{});
+                dma_op(cslot, src, std::integral_constant<int, J0 + i>{}, NotFirst{});
             if constexpr (MD == 2 && i < NCP) {
                 lwrite_op(cslot, std::integral_constant<int, J0 + i>{});
                 gload_op(src, std::integral_constant<int, J0 + i>{}, NotFirst{});
@@ -645,28 +653,46 @@ pipelined_gemm(KArgs args) {
     using Z_ = std::integral_constant<int, 0>;
     constexpr int kNoCopy = 0;
 
-    Frags f0, f1;
-
     // ---- the pipelined K loop ----------------------------------------------------
     //
-    // One k-tile = KSTEPS MFMA stages of 16 k.  Stage kk reads the fragments of
-    // stage kk+1 while the MFMAs of stage kk run.  Before the last stage -- after
-    // this wave's last LDS read of the current slot -- sits the one barrier of the
-    // k-tile: once every wave has passed it, (a) the next k-tile, whose copies this
-    // wave has waited for, is visible to all, and (b) nobody reads the current slot
-    // any more, so it is released and refilled with k-tile t+S while the MFMAs of
-    // the last stage (which read registers, not LDS) still run.  The last stage
-    // also reads the first fragments of the next k-tile, so the matrix pipe has
-    // work across the k-tile boundary.  KSTEPS is even, so stage kk computes from
-    // f0 when kk is even and the last stage from f1.
-    static_assert(KSTEPS % 2 == 0, "fragment double buffer assumes an even k-step count");
-    auto first_stages = [&](const SPG_LDS char* cur) __attribute__((always_inline)) {
-        static_for<0, KSTEPS - 1>([&](auto kc) {
-            constexpr int kk = decltype(kc)::value;
-            if constexpr (kk % 2 == 0) stage(f0, cur, kk + 1, f1, nullptr, kNoCopy, T_{}, M0_{}, Z_{});
-            else stage(f1, cur, kk + 1, f0, nullptr, kNoCopy, T_{}, M0_{}, Z_{});
-        });
+    // One k-tile = KSTEPS MFMA stages of 16 k.  Stage kk computes from fragment set
+    // kk % NF and reads the fragments of stage kk+PF (of the next k-tile once that
+    // passes KSTEPS) into set (kk+PF) % NF.  The one barrier of k-tile t sits before
+    // stage KSTEPS-PF, just after this wave's last LDS read of slot t%S: once every
+    // wave has passed it, (a) k-tile t+1, whose copies this wave has waited for, is
+    // visible to all, and (b) nobody reads slot t%S any more, so it is released
+    // and refilled with k-tile t+S while the last PF stages (whose MFMAs read
+    // registers, not LDS) still run.  Those stages already read k-tile t+1, so the
+    // matrix pipe has work across the k-tile boundary.
+    //
+    // Copies run in windows from one barrier to the next (KSTEPS stages: the last
+    // PF of k-tile t and the first KSTEPS-PF of k-tile t+1).  The window that
+    // starts at barrier t fills slot t%S with k-tile t+S: mode 0 issues all of its
+    // copies in the window's first PF stages, modes 1 and 2 spread them, CPS per
+    // stage (mode 1 writes the k-tile staged in VGPRs and loads the next one into
+    // the freed registers).
+    constexpr int NF = PF == 1 ? 2 : KSTEPS;   // fragment sets
+    static_assert(KSTEPS % NF == 0, "fragment sets must tile the k-steps of a k-tile");
+    Frags fr[NF];
+    auto fset = [&](auto ic) -> Frags& { return fr[decltype(ic)::value % NF]; };
+    using ModeWin = std::integral_constant<int, LDM == 0 ? 1 : (LDM == 1 ? 2 : 3)>;
+    constexpr int WOPS = LDM == 0 ? G::L / PF : CPS;  // copy ops per window stage
+    static_assert(LDM != 0 || G::L % PF == 0, "copies must split over the lookahead stages");
+
+    // stage kk of a k-tile: MFMAs of set kk, reads of step kk+PF from `cur` or `nxt`,
+    // copies of window position `pos` (if any) from `src` into `cslot`
+    auto kstage = [&](auto kc, const SPG_LDS char* cur, const SPG_LDS char* nxt, SPG_LDS char* cslot,
+                      const auto& src, auto pos, auto do_read) __attribute__((always_inline)) {
+        constexpr int kk = decltype(kc)::value;
+        constexpr int rk = kk + PF;
+        constexpr int P = decltype(pos)::value;          // -1: no copies in this stage
+        const SPG_LDS char* rslot = rk < KSTEPS ? cur : nxt;
+        using MD = std::integral_constant<int, P < 0 ? 0 : ModeWin::value>;
+        using J = std::integral_constant<int, (P < 0 ? 0 : P) * WOPS>;
+        stage(fset(kc), rslot, rk % KSTEPS, fset(std::integral_constant<int, rk>{}), cslot, src,
+              do_read, MD{}, J{});
     };
+
     if constexpr (S == 1) {
         // the serial K loop: copy, wait, multiply, and only then let the next copy in
         SPG_LDS char* r0 = slot_of(Z_{});
@@ -674,9 +700,12 @@ pipelined_gemm(KArgs args) {
         for (int t = 0; t < nk; ++t) {
             wait_vmcnt<0>();
             __syncthreads();
-            load_frags(r0, 0, f0);
-            first_stages(r0);
-            stage(f1, nullptr, 0, f0, nullptr, kNoCopy, F_{}, M0_{}, Z_{});
+            load_frags(r0, 0, fr[0]);
+            static_for<0, KSTEPS>([&](auto kc) {
+                constexpr int kk = decltype(kc)::value;
+                using RD = std::integral_constant<bool, kk + 1 < KSTEPS>;
+                kstage(kc, r0, nullptr, nullptr, kNoCopy, std::integral_constant<int, -1>{}, RD{});
+            });
             __syncthreads();
             issue(r0, t + 1, NotFirst{});  // past the last k-tile: zeros
         }
@@ -686,22 +715,23 @@ pipelined_gemm(KArgs args) {
         // needs no branches.
         const int nt = ((nk + S - 1) / S) * S;
         auto first_of = [](auto sc) { return std::integral_constant<bool, decltype(sc)::value == 0>{}; };
+        constexpr int PRE = LDM == 0 ? 0 : PF * CPS;  // ops of k-tile S-1 the window before k-tile 0 moves
         if constexpr (LDM == 0) {
             // prologue: k-tiles 0 .. S-1 fill every slot; wait for k-tile 0
             static_for<0, S>([&](auto sc) { issue(slot_of(sc), sc.value, first_of(sc)); });
             wait_vmcnt<(S - 1) * G::L>();
         } else if constexpr (LDM == 2) {
-            // prologue: k-tiles 0 .. S-2 whole, and the first CPS copies of k-tile S-1
-            // (those the window before k-tile 0 would have issued); wait for k-tile 0
+            // prologue: k-tiles 0 .. S-2 whole, and the copies of k-tile S-1 that the
+            // window before k-tile 0 would have issued; wait for k-tile 0
             static_for<0, S - 1>([&](auto sc) { issue(slot_of(sc), sc.value, first_of(sc)); });
             const DmaSrc src = dma_src(S - 1);
-            static_for<0, CPS>([&](auto jc) {
+            static_for<0, PRE>([&](auto jc) {
                 dma_op(slot_of(std::integral_constant<int, S - 1>{}), src, jc, NotFirst{});
             });
-            wait_vmcnt<(S - 2) * G::L + CPS>();
+            wait_vmcnt<(S - 2) * G::L + PRE>();
         } else {
-            // prologue: k-tiles 0 .. S-2 written, k-tile S-1 staged, its first CPS ops
-            // written and k-tile S loaded in their place (the window before k-tile 0)
+            // prologue: k-tiles 0 .. S-2 written, k-tile S-1 staged, the part of it that
+            // the window before k-tile 0 moves written, and k-tile S loaded in its place
             static_for<0, S - 1>([&](auto sc) {
                 const RegSrc src = reg_src(sc.value);
                 static_for<0, G::L>([&](auto jc) { gload_op(src, jc, first_of(sc)); });
@@ -709,21 +739,15 @@ pipelined_gemm(KArgs args) {
             });
             const RegSrc src1 = reg_src(S - 1), src2 = reg_src(S);
             static_for<0, G::L>([&](auto jc) { gload_op(src1, jc, NotFirst{}); });
-            static_for<0, CPS>([&](auto jc) {
+            static_for<0, PRE>([&](auto jc) {
                 lwrite_op(slot_of(std::integral_constant<int, S - 1>{}), jc);
                 gload_op(src2, jc, NotFirst{});
             });
         }
         lds_barrier();
-        load_frags(slot_of(Z_{}), 0, f0);
+        static_for<0, PF>([&](auto kc) { load_frags(slot_of(Z_{}), kc.value, fset(kc)); });
 
         constexpr int STEADY = (S - 2) * G::L;
-        // k-tile t in slot s.  Direct copies: k-tiles t+1 .. t+S-1 are in flight;
-        // after the barrier slot s is refilled with k-tile t+S (mode 0 all at once,
-        // mode 2 spread over the window up to the next barrier, which also moves
-        // the rest of k-tile t+S-1 into slot s-1).  Register staging: the window
-        // from one barrier to the next writes k-tile t+S into the slot the first
-        // barrier released and loads k-tile t+S+1, CPS ops per stage.
         auto ktile = [&](auto sc, int t) __attribute__((always_inline)) {
             constexpr int s = decltype(sc)::value;
             SPG_LDS char* cur = slot_of(sc);
@@ -734,15 +758,13 @@ pipelined_gemm(KArgs args) {
                 else return dma_src(kt);
             };
             {
-                // register staging writes k-tile t+S-1 into prev and loads k-tile t+S;
-                // spread copies move the rest of k-tile t+S-1 into prev
+                // the window that started at barrier t-1: k-tile t+S-1 into prev
+                // (register staging: write k-tile t+S-1, load k-tile t+S)
                 const auto src = src_of(LDM == 1 ? t + S : t + S - 1);
-                static_for<0, KSTEPS - 1>([&](auto kc) {
+                static_for<0, KSTEPS - PF>([&](auto kc) {
                     constexpr int kk = decltype(kc)::value;
-                    using J = std::integral_constant<int, (kk + 1) * CPS>;
-                    using MD = std::integral_constant<int, LDM == 0 ? 0 : (LDM == 1 ? 2 : 3)>;
-                    if constexpr (kk % 2 == 0) stage(f0, cur, kk + 1, f1, prev, src, T_{}, MD{}, J{});
-                    else stage(f1, cur, kk + 1, f0, prev, src, T_{}, MD{}, J{});
+                    using Pos = std::integral_constant<int, LDM == 0 ? -1 : PF + kk>;
+                    kstage(kc, cur, nxt, prev, src, Pos{}, T_{});
                 });
             }
             if constexpr (LDM != 1) wait_vmcnt<STEADY>();
@@ -750,9 +772,14 @@ pipelined_gemm(KArgs args) {
             // complete in its slot
             lds_barrier();
             {
+                // the window that starts here: k-tile t+S into cur
+                // (register staging: write k-tile t+S, load k-tile t+S+1)
                 const auto src = src_of(LDM == 1 ? t + S + 1 : t + S);
-                using MD = std::integral_constant<int, LDM == 0 ? 1 : (LDM == 1 ? 2 : 3)>;
-                stage(f1, nxt, 0, f0, cur, src, T_{}, MD{}, Z_{});
+                static_for<KSTEPS - PF, KSTEPS>([&](auto kc) {
+                    constexpr int kk = decltype(kc)::value;
+                    using Pos = std::integral_constant<int, kk - (KSTEPS - PF)>;
+                    kstage(kc, cur, nxt, cur, src, Pos{}, T_{});
+                });
             }
         };
         for (int t0 = 0; t0 < nt; t0 += S) {

@@ -3,7 +3,7 @@
 #define SPG_DEFINE_LAUNCHERS
 #include "launch.hpp"
 
-#define SPG_V(unit, BM, BN, BK, WM, WN, S, SWZ, LDM) SPG_V_##unit(BM, BN, BK, WM, WN, S, SWZ, LDM)
+#define SPG_V(unit, BM, BN, BK, WM, WN, S, SWZ, LDM, PF) SPG_V_##unit(BM, BN, BK, WM, WN, S, SWZ, LDM, PF)
 #define SPG_V_0(...)
 #define SPG_V_1(...)
 #define SPG_V_2(...)
@@ -22,4 +22,5 @@
 #define SPG_V_15(...)
 #define SPG_V_16(...)
 #define SPG_V_17(...)
+#define SPG_V_18(...)
 #include "variants.inc"

@@ -10,26 +10,28 @@ namespace spg {
 
 typedef void (*launch_fn)(const KArgs&, dim3, hipStream_t);
 
-template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ, int LDM>
+template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ, int LDM,
+          int PF>
 void launch_pipelined(const KArgs& a, dim3 grid, hipStream_t st);
 
 #ifdef SPG_DEFINE_LAUNCHERS
-template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ, int LDM>
+template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ, int LDM,
+          int PF>
 void launch_pipelined(const KArgs& a, dim3 grid, hipStream_t st) {
     using G = Geom<BM, BN, BK, WM, WN, S>;
-    hipLaunchKernelGGL((pipelined_gemm<BF16, B_NK, BM, BN, BK, WM, WN, S, SWZ, LDM>), grid,
+    hipLaunchKernelGGL((pipelined_gemm<BF16, B_NK, BM, BN, BK, WM, WN, S, SWZ, LDM, PF>), grid,
                        dim3(G::NT), 0, st, a);
 }
 #endif
 
 }  // namespace spg
 
-#define SPG_INSTANTIATE_ALL(BM, BN, BK, WM, WN, S, SWZ, LDM)                                        \
-    template void spg::launch_pipelined<false, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM>(     \
+#define SPG_INSTANTIATE_ALL(BM, BN, BK, WM, WN, S, SWZ, LDM, PF)                                        \
+    template void spg::launch_pipelined<false, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF>(     \
         const spg::KArgs&, dim3, hipStream_t);                                                     \
-    template void spg::launch_pipelined<false, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM>(      \
+    template void spg::launch_pipelined<false, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF>(      \
         const spg::KArgs&, dim3, hipStream_t);                                                     \
-    template void spg::launch_pipelined<true, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM>(      \
+    template void spg::launch_pipelined<true, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF>(      \
         const spg::KArgs&, dim3, hipStream_t);                                                     \
-    template void spg::launch_pipelined<true, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM>(       \
+    template void spg::launch_pipelined<true, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF>(       \
         const spg::KArgs&, dim3, hipStream_t);
