@@ -771,6 +771,11 @@ pipelined_gemm(KArgs args) {
             // every wave has finished reading slot s (released) and the next k-tile is
             // complete in its slot
             lds_barrier();
+            // The stages after the barrier run at raised wave priority: with two waves
+            // per SIMD the one that passed the barrier first keeps the matrix pipe
+            // while its partner is still in the barrier's wake (measured +1.7% at
+            // 8192^3 with 128x64 wave tiles).
+            __builtin_amdgcn_s_setprio(1);
             {
                 // the window that starts here: k-tile t+S into cur
                 // (register staging: write k-tile t+S, load k-tile t+S+1)
@@ -781,6 +786,7 @@ pipelined_gemm(KArgs args) {
                     kstage(kc, cur, nxt, cur, src, Pos{}, T_{});
                 });
             }
+            __builtin_amdgcn_s_setprio(0);
         };
         for (int t0 = 0; t0 < nt; t0 += S) {
             static_for<0, S>([&](auto sc) { ktile(sc, t0 + decltype(sc)::value); });
