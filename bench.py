@@ -65,6 +65,67 @@ def time_gemm(w, steps, warmup, force=None):
     return wall_ms, kern_ms, cfg
 
 
+def sustained_clock(w, seconds=2.0):
+    """Runs the workload back to back for `seconds` while sampling the engine clock the
+    SMU reports (rocm-smi); returns (median MHz, kernel us at that time) or None."""
+    import json as _json
+    import subprocess
+    import threading
+
+    import numpy as np
+    import torch
+
+    import software_pipelined_tiled_gemm_amd as spg
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    a, b = W.make_inputs(w)
+    A = torch.from_numpy(a.view(np.int16)).to(dev)
+    B = torch.from_numpy(b.view(np.int16)).to(dev)
+    C = torch.empty((w.M, w.N), dtype=torch.int16 if w.out_dtype != W.F32 else torch.float32,
+                    device=dev)
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                                   text=True, timeout=10)
+                for card in _json.loads(r.stdout).values():
+                    v = str(card.get("sclk clock speed:", ""))
+                    if "Mhz" in v:
+                        samples.append(float(v.strip("()Mhz")))
+            except Exception:
+                return
+            time.sleep(0.2)
+
+    g = spg.Gemm(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.b_layout, w.epilogue)
+    for _ in range(10):
+        g(A, B, C)
+    torch.cuda.synchronize(dev)
+    th = threading.Thread(target=sample)
+    th.start()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0, n = time.time(), 0
+    e0.record()
+    while time.time() - t0 < seconds:
+        for _ in range(25):
+            g(A, B, C)
+        n += 25
+        torch.cuda.synchronize(dev)
+    e1.record()
+    torch.cuda.synchronize(dev)
+    stop.set()
+    th.join()
+    g.close()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    if len(samples) < 3:
+        return None
+    samples = sorted(samples[1:])
+    return samples[len(samples) // 2], us
+
+
 def cpu_baseline(w, target_s=15.0):
     """The oracle (fp64 triple loop, OpenMP over rows) on a bounded sample of rows."""
     import numpy as np
@@ -165,7 +226,8 @@ def main():
     ap.add_argument("--tile", default=None,
                     help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging[:WMxWN[:lookahead]]]]] "
                          "(default: the library's choice)")
-    ap.add_argument("--no-extra", action="store_true", help="skip the fp16 8192^3 extra line")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the extra lines (fp16 8192^3, the 8-GPU shard, the sustained clock)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy 5 times, so that HBM "
                          "byte counters can be scaled against a kernel of known traffic")
@@ -199,6 +261,23 @@ def main():
         extra["nn_f16_8192"] = {"tflops": round(w16.flops / (k16 * 1e-3) / 1e12, 2),
                                 "kernel_us": round(k16 * 1e3, 2), "config": cfg16.as_dict()}
         log(f"  fp16 8192^3: {extra['nn_f16_8192']}")
+        # one GPU's share of the 8-GPU row split (A and C by rows, B replicated)
+        wsh = W.custom(w.M // 8, w.N, w.K, w.in_dtype, w.out_dtype, w.b_layout, w.epilogue,
+                       name="nn_bf16_8192_shard_of_8")
+        _, ksh, cfgsh = time_gemm(wsh, args.steps, args.warmup)
+        extra[wsh.name] = {"M": wsh.M, "N": wsh.N, "K": wsh.K,
+                           "tflops": round(wsh.flops / (ksh * 1e-3) / 1e12, 2),
+                           "kernel_us": round(ksh * 1e3, 2), "config": cfgsh.as_dict()}
+        log(f"  shard of 8: {extra[wsh.name]}")
+        clk = sustained_clock(w)
+        if clk is not None:
+            mhz, us = clk
+            tf = w.flops / (us * 1e-6) / 1e12
+            extra["sustained_clock"] = {
+                "sclk_mhz_median": mhz, "kernel_us": round(us, 2), "tflops": round(tf, 2),
+                "mfma_busy_at_that_clock": round(tf / (PEAK_TFLOPS[w.in_dtype] * mhz / 2400.0), 4),
+                "note": "2 s back-to-back run, clock sampled with rocm-smi; peak scales with clock"}
+            log(f"  sustained: {extra['sustained_clock']}")
 
     if args.copy_calibration:
         src = torch.empty(128 << 20, dtype=torch.int16, device="cuda:0").fill_(1)

@@ -124,15 +124,27 @@ const Variant* find_cfg(int bm, int bn, int bk, int stages, int staging, int wm,
 }
 
 gemm_tile_config heuristic(int64_t M, int64_t N) {
-    // Prefer the largest tile (least L2->LDS traffic per flop) that still gives
-    // every CU at least one tile; MI355X has 256 CUs.
-    auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    // Estimated time of a candidate = rounds of the 256 CUs it needs x its tile's
+    // area / its measured per-tile throughput relative to 256x256 (bf16 NN 8192^3
+    // and the 1024x8192x8192 shard on MI355X: 256x128 runs at 0.91 of the 256x256
+    // rate per output, 128x128 at 0.66).  The smallest estimate wins: 256x256 as long
+    // as the grid is not much less than one round, 256x128 for half-size grids,
+    // 128x128 for small problems.
     const int64_t cus = 256;
-    gemm_tile_config c;
-    // 256x256 tiles with 8 waves (two per SIMD, 128x64 each) measured best at 8192^3
-    if (tiles(256, 256) >= cus) c = find_cfg(256, 256, 64, 2, 0, 128, 64)->cfg;
-    else c = find_cfg(128, 128, 64, 3, 0, 64, 64)->cfg;
-    c.group_m = 8;
+    struct Cand { int bm, bn, bk, st, wm, wn; double eff; };
+    const Cand cands[] = {{256, 256, 64, 2, 128, 64, 1.0},
+                          {256, 128, 64, 3, 64, 64, 0.91},
+                          {128, 128, 64, 3, 64, 64, 0.66}};
+    const Cand* best = nullptr;
+    double best_t = 0.0;
+    for (const Cand& c : cands) {
+        const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+        const double t = (double)((tiles + cus - 1) / cus) * c.bm * c.bn / c.eff;
+        if (!best || t < best_t) { best = &c; best_t = t; }
+    }
+    gemm_tile_config c = find_cfg(best->bm, best->bn, best->bk, best->st, 0, best->wm, best->wn)->cfg;
+    // 8 tile rows per raster group on tall grids; 4 on grids of at most 16 tile rows
+    c.group_m = (M + best->bm - 1) / best->bm > 16 ? 8 : 4;
     c.xcd_remap = 1;
     return c;
 }

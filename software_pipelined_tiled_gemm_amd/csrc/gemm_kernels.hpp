@@ -600,7 +600,7 @@ pipelined_gemm(KArgs args) {
 #endif
     constexpr int RPS = SPG_READS_PER_STEP;  // LDS reads issued per MFMA step
     constexpr int CPS = G::L / KSTEPS;       // copy ops per stage when spread over a window
-    static_assert(G::L % KSTEPS == 0, "copy ops must split evenly over the stages");
+    static_assert(LDM == 0 || G::L % KSTEPS == 0, "copy ops must split evenly over the stages");
     // One MFMA stage with its memory traffic interleaved: step i issues MFMA i of
     // `now`, then copy op i and RPS LDS reads of the next stage (into `nx`, from
     // `rslot` at k-step rkk).  Copy modes: 1, all L direct-to-LDS ops of the k-tile

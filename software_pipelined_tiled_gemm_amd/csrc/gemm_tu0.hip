@@ -23,4 +23,6 @@
 #define SPG_V_16(...)
 #define SPG_V_17(...)
 #define SPG_V_18(...)
+#define SPG_V_19(...)
+#define SPG_V_20(...)
 #include "variants.inc"

@@ -141,6 +141,14 @@ def test_heuristic_tiles(L):
         spg.gemm_destroy(h)
         return c
     big = cfg(8192, 8192, 8192)
-    assert (big.block_m, big.block_n) in ((256, 256), (256, 128), (128, 256))
+    assert (big.block_m, big.block_n, big.wave_m, big.wave_n) == (256, 256, 128, 64)
     small = cfg(256, 256, 256)
     assert (small.block_m, small.block_n) == (128, 128)
+    # the cost model: rounds of 256 CUs x tile area / per-tile throughput
+    shard = cfg(1024, 8192, 8192)           # 128 tiles of 256x256, 256 of 256x128
+    assert (shard.block_m, shard.block_n) == (256, 128)
+    gelu = cfg(3072, 4096, 4096)            # 192 tiles of 256x256: one round
+    assert (gelu.block_m, gelu.block_n) == (256, 256)
+    ragged = cfg(3000, 5000, 1000)          # 12 x 20 = 240 tiles of 256x256
+    assert (ragged.block_m, ragged.block_n) == (256, 256)
+    assert cfg(4096, 4096, 4096).group_m == 4 and big.group_m == 8
