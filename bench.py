@@ -5,7 +5,7 @@ Workload (one "step" = one GEMM over resident inputs): M = N = K = 8192, bf16 A
 fp32 accumulation, bf16 output.  The same problem in fp16 is timed too and
 reported under "extra".  Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps 200] [--warmup 500] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -218,8 +218,10 @@ def parse_tile(spec):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the GPU leaves its idle clock state over the first ~0.1-0.3 s of work: the
+    # default warm-up (500 launches, ~0.4 s at 8192^3) lets it settle first
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="nn_bf16_8192",
                     help="workload name from workloads.WORKLOADS")
