@@ -29,7 +29,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
 LAYOUTS = {"kn": 0, "nk": 1}
-EPILOGUES = {"none": 0, "gelu_tanh": 1}
+EPILOGUES = {"none": 0, "gelu_tanh": 1, "relu": 2}
 
 
 def compile_source(src: str, out: str) -> str:

@@ -16,7 +16,10 @@
  *     0.5 x (1 + tanh(0.7978845608 (x + 0.044715 x^3))), the function the
  *     XLA:GPU emitters page fuses in its loop-emitter example and the
  *     Triton lecture notes write in their GeLU kernel; the constants are
- *     the fp32 ones (sqrt(2/pi) and 0.044715), evaluated in double.
+ *     the fp32 ones (sqrt(2/pi) and 0.044715), evaluated in double; or ReLU,
+ *     max(x, 0), which the Triton lecture notes' matmul kernel applies to its
+ *     accumulator before the store (Matmul section); zero of either sign
+ *     maps to +0.
  * Output encodings (binary16, bfloat16, binary32) round the double result to
  * nearest, ties to even, straight from double (no double rounding).
  *
@@ -38,7 +41,7 @@ enum { OR_F16 = 0, OR_BF16 = 1, OR_F32 = 2 };
 /* B storage codes */
 enum { OR_B_KN = 0, OR_B_NK = 1 };
 /* epilogue codes */
-enum { OR_EPI_NONE = 0, OR_EPI_GELU_TANH = 1 };
+enum { OR_EPI_NONE = 0, OR_EPI_GELU_TANH = 1, OR_EPI_RELU = 2 };
 
 /* ---- exact decoders ------------------------------------------------------ */
 
@@ -119,6 +122,10 @@ double oracle_gelu_tanh(double x) {
     return 0.5 * x * (1.0 + tanh(0.7978845608 * (x + 0.044715 * x * x * x)));
 }
 
+/* ---- ReLU ----------------------------------------------------------------- */
+
+double oracle_relu(double x) { return x > 0.0 ? x : 0.0; }
+
 /* ---- vector helpers for the Python side -------------------------------- */
 
 void oracle_decode_array(const uint16_t* bits, int64_t n, int dtype, double* out) {
@@ -153,7 +160,8 @@ int oracle_gemm_rows(const uint16_t* A, const uint16_t* B, int64_t M, int64_t N,
     if (M < 0 || N < 0 || K < 0 || nrows < 0) return -1;
     if (in_dtype != OR_F16 && in_dtype != OR_BF16) return -1;
     if (b_layout != OR_B_KN && b_layout != OR_B_NK) return -1;
-    if (epilogue != OR_EPI_NONE && epilogue != OR_EPI_GELU_TANH) return -1;
+    if (epilogue != OR_EPI_NONE && epilogue != OR_EPI_GELU_TANH && epilogue != OR_EPI_RELU)
+        return -1;
     if (rows == NULL && nrows != M) return -1;
     if (rows != NULL)
         for (int64_t r = 0; r < nrows; ++r)
@@ -181,6 +189,8 @@ int oracle_gemm_rows(const uint16_t* A, const uint16_t* B, int64_t M, int64_t N,
         }
         if (epilogue == OR_EPI_GELU_TANH)
             for (int64_t j = 0; j < N; ++j) c[j] = oracle_gelu_tanh(c[j]);
+        else if (epilogue == OR_EPI_RELU)
+            for (int64_t j = 0; j < N; ++j) c[j] = oracle_relu(c[j]);
     }
     free(Bd);
     return 0;

@@ -310,6 +310,36 @@ def pin_rows_and_epilogue(o):
     assert np.all(Z == 0)
 
 
+def pin_relu(o):
+    """ReLU epilogue (the Triton lecture notes' matmul kernel, maximum(acc, 0)): with A = I
+    it is max(b, 0) of every element of B exactly; relu(c) - relu(-c) = c, so the ReLU
+    results for A and -A differ by exactly the plain result; relu of the empty sum is 0."""
+    r = _rng(12)
+    K, N = 16, 21
+    Bv = r.uniform(-3, 3, (K, N))
+    Bv[0, :5] = 0.0
+    for dtype in ("f16", "bf16"):
+        Bb = _enc(o, Bv, dtype)
+        eye = _enc(o, np.eye(K), dtype)
+        for layout in ("kn", "nk"):
+            C = o.gemm(eye, _store_b(Bb, layout), K, N, K, dtype, layout, epilogue="relu")
+            Bd = o.decode(Bb, dtype)
+            assert np.array_equal(C, np.where(Bd > 0, Bd, 0.0))
+            assert np.any(C == 0) and np.any(C > 0)
+    M, N, K = 10, 13, 37
+    Av = r.normal(0, 1, (M, K))
+    Ab, Anb = _enc(o, Av, "bf16"), _enc(o, -Av, "bf16")
+    Bb = _enc(o, r.normal(0, 1, (K, N)), "bf16")
+    plain = o.gemm(Ab, Bb, M, N, K, "bf16", "kn")
+    pos = o.gemm(Ab, Bb, M, N, K, "bf16", "kn", epilogue="relu")
+    neg = o.gemm(Anb, Bb, M, N, K, "bf16", "kn", epilogue="relu")
+    assert np.array_equal(pos - neg, plain)
+    assert np.all(pos >= 0) and np.any(plain < 0)
+    Z = o.gemm(np.zeros((2, 0), np.uint16), np.zeros((0, 3), np.uint16), 2, 3, 0, "f16", "kn",
+               epilogue="relu")
+    assert np.all(Z == 0)
+
+
 def pin_small_exact_integers(o):
     """Integer-valued inputs: C equals numpy's integer matmul exactly (no rounding anywhere)."""
     r = _rng(11)
@@ -338,5 +368,6 @@ ALL_PINS = [
     pin_layout_equivalence,
     pin_zero_padding,
     pin_rows_and_epilogue,
+    pin_relu,
     pin_small_exact_integers,
 ]

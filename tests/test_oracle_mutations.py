@@ -35,6 +35,10 @@ MUTATIONS = {
     "gelu_dropped_cubic": ("(x + 0.044715 * x * x * x)", "(x)"),
     "gelu_sign": ("(1.0 + tanh(", "(1.0 - tanh("),
     "epilogue_skipped": ("c[j] = oracle_gelu_tanh(c[j]);", "c[j] = c[j];"),
+    "relu_as_abs": ("return x > 0.0 ? x : 0.0;", "return fabs(x);"),
+    "relu_keeps_negatives": ("return x > 0.0 ? x : 0.0;", "return x < 0.0 ? x : 0.0;"),
+    "relu_threshold_one": ("return x > 0.0 ? x : 0.0;", "return x > 1.0 ? x : 0.0;"),
+    "relu_skipped": ("c[j] = oracle_relu(c[j]);", "c[j] = c[j];"),
 }
 
 
