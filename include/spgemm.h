@@ -55,7 +55,12 @@ typedef enum {
     GEMM_B_NK = 1  /* B row-major [N,K]  ("TN", transpose_B) */
 } gemm_b_layout;
 
-typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1 } gemm_epilogue;
+/* Epilogue applied to the fp32 accumulator before the output conversion:
+ *   GEMM_EPI_GELU_TANH  the tanh approximation of GELU above;
+ *   GEMM_EPI_RELU       max(x, 0), what the Triton lecture notes' matmul kernel
+ *                       (Matmul section, matmul_relu_kernel) applies to its
+ *                       accumulator before the store; -0 becomes +0. */
+typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1, GEMM_EPI_RELU = 2 } gemm_epilogue;
 
 /* Tile configuration of the pipelined kernel.
  *   block_m x block_n   output tile of one workgroup (128 or 256 each)

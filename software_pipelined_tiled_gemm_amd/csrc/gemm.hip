@@ -230,7 +230,8 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
     if (!valid_dtype_in((int)in_dtype) || !valid_dtype_out((int)out_dtype)) return GEMM_ERR_INVALID_ARG;
     if (b_layout != GEMM_B_KN && b_layout != GEMM_B_NK) return GEMM_ERR_INVALID_ARG;
-    if (epilogue != GEMM_EPI_NONE && epilogue != GEMM_EPI_GELU_TANH) return GEMM_ERR_INVALID_ARG;
+    if (epilogue != GEMM_EPI_NONE && epilogue != GEMM_EPI_GELU_TANH && epilogue != GEMM_EPI_RELU)
+        return GEMM_ERR_INVALID_ARG;
 
     const Variant* var = nullptr;
     gemm_tile_config cfg;

@@ -36,7 +36,7 @@
 //    output columns, which lets the epilogue pack 4 outputs per LDS write.
 //  * B stored [K,N] (N contiguous) is read with ds_read_b64_tr_b16, the
 //    gfx950 transposing LDS read, instead of being transposed in registers.
-//  * Epilogue: optional GELU on the fp32 accumulator, round-to-nearest-even
+//  * Epilogue: optional GELU or ReLU on the fp32 accumulator, round-to-nearest-even
 //    conversion, staging through LDS (aliasing the drained ring), and 16-byte
 //    row-contiguous global stores (the coalesced linear output traversal of
 //    the XLA:GPU emitters page, loop emitter, with wider vectors).
@@ -73,7 +73,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past any num_records: loads 0
 
 enum { kOutF16 = 0, kOutBF16 = 1, kOutF32 = 2 };
-enum { kEpiNone = 0, kEpiGelu = 1 };
+enum { kEpiNone = 0, kEpiGelu = 1, kEpiRelu = 2 };
 
 struct KArgs {
     const uint16_t* A;
@@ -157,8 +157,19 @@ __device__ __forceinline__ float gelu_tanh(float x) {
     return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// max(x, 0) as the Triton lecture notes' matmul kernel applies it to the accumulator;
+// a select (not fmaxf) so that -0 becomes +0 and the result is fully determined
+__device__ __forceinline__ float relu(float x) { return x > 0.0f ? x : 0.0f; }
+
+template <int EPI>
+__device__ __forceinline__ float epi_t(float x) {
+    if constexpr (EPI == kEpiGelu) return gelu_tanh(x);
+    else if constexpr (EPI == kEpiRelu) return relu(x);
+    else return x;
+}
+
 __device__ __forceinline__ float epi_apply(float x, int epi) {
-    return epi == kEpiGelu ? gelu_tanh(x) : x;
+    return epi == kEpiGelu ? gelu_tanh(x) : (epi == kEpiRelu ? relu(x) : x);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bits(float x, bool bf16) {
@@ -204,12 +215,12 @@ __device__ __forceinline__ floatx16 mfma(const u32x4& x, const u32x4& y, const f
 // the pipelined kernel
 // ---------------------------------------------------------------------------
 
-// Epilogue of one wave: accumulator -> (GELU) -> output type -> LDS staging ->
+// Epilogue of one wave: accumulator -> (GELU / ReLU) -> output type -> LDS staging ->
 // 16-byte row-contiguous global stores.  The wave's C tile is processed 32 rows
 // (one MFMA block row) at a time through a private 32 x WN staging buffer whose
 // 16-B chunks are XOR-swizzled by row so that both the 4-value writes (32 rows,
 // same column) and the row reads are free of bank conflicts.
-template <int OD, bool GELU, int TM, int TN, int WN>
+template <int OD, int EPI, int TM, int TN, int WN>
 __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TN][TM], char* stg,
                                            const KArgs& args, int m_base, int n_base, int lane) {
     constexpr int OB = OD == kOutF32 ? 4 : 2;         // output bytes
@@ -232,7 +243,7 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TN][TM], char* 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     v[e] = acc[bn][bm][4 * q + e];
-                    if constexpr (GELU) v[e] = gelu_tanh(v[e]);
+                    v[e] = epi_t<EPI>(v[e]);
                 }
                 const int byte = (bn * 32 + 8 * q + 4 * (lane >> 5)) * OB;
                 char* dst = stg + lrow * ROWB + (((byte >> 4) ^ swz(lrow)) << 4) + (byte & 15);
@@ -807,18 +818,17 @@ pipelined_gemm(KArgs args) {
     }
     // one branch on the (uniform) output type and epilogue, outside all accumulator reads
     const int od = args.out_dtype;
-    const bool ge = args.epilogue == kEpiGelu;
+    const int ep = args.epilogue;
     const int m_base = m0 + wm * WM, n_base = n0 + wn * WN;
-    if (od == kOutF32) {
-        if (ge) store_tile<kOutF32, true, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
-        else store_tile<kOutF32, false, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
-    } else if (od == kOutBF16) {
-        if (ge) store_tile<kOutBF16, true, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
-        else store_tile<kOutBF16, false, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
-    } else {
-        if (ge) store_tile<kOutF16, true, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
-        else store_tile<kOutF16, false, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
-    }
+    auto store_as = [&](auto odc) __attribute__((always_inline)) {
+        constexpr int OD = decltype(odc)::value;
+        if (ep == kEpiGelu) store_tile<OD, kEpiGelu, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+        else if (ep == kEpiRelu) store_tile<OD, kEpiRelu, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+        else store_tile<OD, kEpiNone, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+    };
+    if (od == kOutF32) store_as(std::integral_constant<int, kOutF32>{});
+    else if (od == kOutBF16) store_as(std::integral_constant<int, kOutBF16>{});
+    else store_as(std::integral_constant<int, kOutF16>{});
 }
 
 // ---------------------------------------------------------------------------

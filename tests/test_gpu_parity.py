@@ -51,8 +51,27 @@ def test_all_variants_ragged(in_dtype, b_layout):
         assert np.array_equal(v, vals[0])
 
 
+@pytest.mark.parametrize("out_dtype", [W.BF16, W.F32])
+def test_relu_every_wave_tile(out_dtype):
+    # the epilogue is instantiated per (output type, epilogue, wave tile): run ReLU on one
+    # configuration of every distinct block and wave tile, ragged in M, N and K
+    w = W.custom(520, 648, 616, W.F16, out_dtype, W.B_KN, "relu", ("uniform", -1.0, 1.0))
+    a, b = W.make_inputs(w)
+    seen = set()
+    for cfg in _variants():
+        key = (cfg.block_m, cfg.block_n, cfg.wave_m, cfg.wave_n)
+        if key in seen:
+            continue
+        seen.add(key)
+        _log(f"relu {cfg} {w.describe()}")
+        C, _ = G.run(w, a, b, force=cfg)
+        got = G.c_values(C, w)
+        G.check(w, a, b, got)
+        assert np.all(got >= 0) and np.any(got == 0) and np.any(got > 0)
+
+
 @pytest.mark.parametrize("out_dtype", [W.F16, W.BF16, W.F32])
-@pytest.mark.parametrize("epilogue", ["none", "gelu_tanh"])
+@pytest.mark.parametrize("epilogue", ["none", "gelu_tanh", "relu"])
 def test_output_dtypes_and_epilogue(out_dtype, epilogue):
     for b_layout in (W.B_KN, W.B_NK):
         w = W.custom(384, 392, 320, W.BF16, out_dtype, b_layout, epilogue, ("normal", 0.3))
@@ -86,7 +105,7 @@ def _small_cases():
 @pytest.mark.parametrize("in_dtype", [W.F16, W.BF16])
 def test_small_shapes(b_layout, in_dtype):
     for (M, N, K) in _small_cases():
-        for out_dtype, epi in ((in_dtype, "none"), (W.F32, "gelu_tanh")):
+        for out_dtype, epi in ((in_dtype, "none"), (W.F32, "gelu_tanh"), (in_dtype, "relu")):
             w = W.custom(M, N, K, in_dtype, out_dtype, b_layout, epi)
             a, b = W.make_inputs(w)
             C, cfg = G.run(w, a, b)
@@ -101,7 +120,7 @@ def test_empty_and_k_zero():
         a, b = W.make_inputs(w)
         G.run(w, a, b)
     # K == 0: C = epi(0) = 0 everywhere, written over a non-zero fill
-    for epi in ("none", "gelu_tanh"):
+    for epi in ("none", "gelu_tanh", "relu"):
         w = W.custom(40, 24, 0, W.BF16, W.F32, W.B_KN, epi)
         a, b = W.make_inputs(w)
         C = G.alloc_c(w, fill=7)
@@ -153,6 +172,7 @@ def test_autotune_keeps_parity():
 # ---------------------------------------------------------------------------
 
 FULL = ["tn_f16_256", "tn_f16_3000x5000x1000_f32out", "pallas_hopper_example",
+        "nn_f16_2048x2048x1024_relu_f32out",
         "tn_f16_4096", "nn_bf16_3072x4096x4096_gelu", "nn_bf16_8192", "nn_f16_8192"]
 SAMPLE_ROWS = {"tn_f16_4096": 96, "nn_bf16_3072x4096x4096_gelu": 96, "nn_bf16_8192": 48,
                "nn_f16_8192": 48}

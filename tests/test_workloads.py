@@ -47,3 +47,4 @@ def test_workload_table():
     assert (t["nn_bf16_8192"].M, t["nn_bf16_8192"].b_layout) == (8192, W.B_KN)
     assert t["tn_f16_3000x5000x1000_f32out"].out_dtype == W.F32
     assert t["nn_bf16_3072x4096x4096_gelu"].epilogue == "gelu_tanh"
+    assert t["nn_f16_2048x2048x1024_relu_f32out"].epilogue == "relu"

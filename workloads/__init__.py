@@ -58,7 +58,8 @@ class Workload:
 
 
 # The five workloads of the benchmark table plus the Pallas guide's Hopper
-# example shape (m = 132*128, n = 4*128, k = 10*64, uniform [0, 1) fp16).
+# example shape (m = 132*128, n = 4*128, k = 10*64, uniform [0, 1) fp16) and a
+# matmul + ReLU case after the Triton lecture notes.
 WORKLOADS: Dict[str, Workload] = {
     w.name: w
     for w in (
@@ -71,6 +72,10 @@ WORKLOADS: Dict[str, Workload] = {
                  ("normal", 0.02)),
         Workload("pallas_hopper_example", 132 * 128, 4 * 128, 10 * 64, F16, F16, B_KN, "none",
                  ("unit",)),
+        # The Triton lecture notes' matmul + ReLU (B stored [K,N], fp32 output; the notes
+        # give no size, this one spans 8 x 8 tiles of 256).
+        Workload("nn_f16_2048x2048x1024_relu_f32out", 2048, 2048, 1024, F16, F32, B_KN, "relu",
+                 ("uniform", -1.0, 1.0)),
         # The same 8192^3 problem in fp16 (the metric's wording names fp16).
         Workload("nn_f16_8192", 8192, 8192, 8192, F16, F16, B_KN, "none", ("uniform", -1.0, 1.0)),
     )
