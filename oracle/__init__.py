@@ -102,6 +102,16 @@ class Oracle:
                                    out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
         return out
 
+    def gelu_elementwise(self, x_bits: np.ndarray, dtype: str) -> np.ndarray:
+        """The standalone GELU on stored elements: exact decode, gelu in double.
+        x_bits are uint16 patterns (f16/bf16) or uint32 patterns (f32); returns the
+        unrounded double results (self.encode gives the correctly rounded patterns)."""
+        if dtype == "f32":
+            x = np.ascontiguousarray(x_bits, dtype=np.uint32).view(np.float32).astype(np.float64)
+        else:
+            x = self.decode(np.ascontiguousarray(x_bits, dtype=np.uint16), dtype)
+        return self.gelu(x)
+
     def gemm(self, A_bits: np.ndarray, B_bits: np.ndarray, M: int, N: int, K: int,
              in_dtype: str, b_layout: str, epilogue: str = "none",
              rows: Optional[Sequence[int]] = None) -> np.ndarray:
@@ -165,6 +175,10 @@ def round_to(x, dtype):
 
 def gelu(x):
     return default().gelu(x)
+
+
+def gelu_elementwise(x_bits, dtype):
+    return default().gelu_elementwise(x_bits, dtype)
 
 
 def gemm(A_bits, B_bits, M, N, K, in_dtype, b_layout, epilogue="none", rows=None):

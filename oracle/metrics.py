@@ -61,3 +61,31 @@ def compare(C: np.ndarray, C_ref: np.ndarray, out_dtype: str, s: float) -> dict:
     gate = err_lit if out_dtype == "f32" else err_q
     return {"err_lit": err_lit, "err_q": err_q, "floor": floor, "tol": tol,
             "ok": bool(nonfinite == 0 and gate <= tol), "nonfinite": nonfinite}
+
+
+# Standalone elementwise GELU (fp32 evaluation, round to nearest even):
+#   |y - g| <= ulp_out(g)/2 + EW_REL |g| + EW_ABS
+# with g the exact (double) gelu of the stored input.  EW_REL bounds the fp32
+# evaluation: the exponent argument -2 log2(e) u carries ~3 roundings, and an
+# argument error of d moves exp2 by ln(2) |t| d relatively, |t| <= 128 before the
+# fp32 exponent overflows: 128 * 0.69 * 3 * 2^-24 + 2 * 2^-24 < 2^-16.  EW_ABS covers
+# the far negative side where exp2 overflows and the fp32 result is 0 while the
+# exact value is a (sub)normal below 2^-120.
+EW_REL = 2.0 ** -16
+EW_ABS = 2.0 ** -120
+
+
+def compare_elementwise(y: np.ndarray, g: np.ndarray, out_dtype: str) -> dict:
+    """Worst excess over the elementwise GELU bound (<= 0 passes), NaN agreement, and
+    the fraction of results equal to the correctly rounded exact value."""
+    y = np.asarray(y, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    nan_y, nan_g = np.isnan(y), np.isnan(g)
+    fin = ~nan_g & np.isfinite(g)
+    inf_ok = bool(np.all(y[np.isinf(g)] == g[np.isinf(g)]))
+    d = np.abs(y[fin] - g[fin])
+    bound = 0.5 * ulp(g[fin], out_dtype) + EW_REL * np.abs(g[fin]) + EW_ABS
+    excess = float(np.max(d - bound)) if d.size else -1.0
+    exact = float(np.mean(y[fin] == round_to(g[fin], out_dtype))) if d.size else 1.0
+    return {"excess": excess, "nan_match": bool(np.array_equal(nan_y, nan_g)), "inf_ok": inf_ok,
+            "exact_frac": exact, "ok": excess <= 0.0 and bool(np.array_equal(nan_y, nan_g)) and inf_ok}

@@ -10,6 +10,7 @@ least one pin.
 
 from __future__ import annotations
 
+import decimal
 import math
 import os
 import struct
@@ -182,6 +183,25 @@ def pin_gelu(o):
     assert abs(consts["sqrt_2_over_pi"] - math.sqrt(2.0 / math.pi)) < 1e-15
     # gelu is increasing above its minimum near x = -0.75 and its minimum is about -0.17
     assert -0.18 < g.min() < -0.16
+    # the literal form 0.5 x (1 + tanh u) with Python's tanh, where it is well
+    # conditioned (1 + tanh u >= 2e-3)
+    for v in np.linspace(-3.0, 12.0, 301):
+        u = 0.7978845608 * (v + 0.044715 * v ** 3)
+        assert abs(o.gelu(np.array([v]))[0] - 0.5 * v * (1.0 + math.tanh(u))) <= 1e-14
+    # the negative tail, where 1 + tanh u cancels in double: the literal definition in
+    # 120-digit decimal arithmetic (1 + tanh u ~ 1e-50 at x = -13), tanh from its
+    # exponential definition
+    with decimal.localcontext() as ctx:
+        ctx.prec = 120
+        for v in (-4.0, -5.5, -6.9375, -7.0625, -8.0, -9.5, -11.0, -13.0):
+            d = decimal.Decimal(v)
+            u = decimal.Decimal("0.7978845608") * (d + decimal.Decimal("0.044715") * d ** 3)
+            e2 = (2 * u).exp()
+            ref = decimal.Decimal("0.5") * d * (1 + (e2 - 1) / (e2 + 1))
+            got = o.gelu(np.array([v]))[0]
+            # the rounding of u in double moves exp(-2u) by ~2|u| 2^-53 relatively
+            rel = decimal.Decimal(1e-15) * (1 + abs(u))
+            assert abs(decimal.Decimal(got) - ref) <= abs(ref) * rel, (v, got, ref)
 
 
 # ---------------------------------------------------------------------------
@@ -340,6 +360,23 @@ def pin_relu(o):
     assert np.all(Z == 0)
 
 
+def pin_gelu_elementwise(o):
+    """The standalone GELU on stored elements: 0 -> 0; for bf16 x >= 8 the exact result
+    rounds back to x itself (gelu(x) = x sigmoid(2u) with 1 - sigmoid(2u) < 2^-40), for
+    x <= -12 to -0 (|gelu(x)| < 2^-400); the fp32 path decodes binary32 exactly."""
+    for dtype in ("f16", "bf16"):
+        vals = np.array([0.0, 8.0, 9.5, 100.0, 1000.0, -12.0, -20.0, -1000.0])
+        bits = _enc(o, vals, dtype)
+        g = o.gelu_elementwise(bits, dtype)
+        out = o.encode(g, dtype)
+        assert out[0] == 0
+        assert np.array_equal(out[1:5], bits[1:5])
+        assert np.all(out[5:] == 0x8000)
+    x32 = np.array([0.5, -0.5, 3.0], dtype=np.float32)
+    g = o.gelu_elementwise(x32.view(np.uint32), "f32")
+    assert np.array_equal(g, o.gelu(x32.astype(np.float64)))
+
+
 def pin_small_exact_integers(o):
     """Integer-valued inputs: C equals numpy's integer matmul exactly (no rounding anywhere)."""
     r = _rng(11)
@@ -369,5 +406,6 @@ ALL_PINS = [
     pin_zero_padding,
     pin_rows_and_epilogue,
     pin_relu,
+    pin_gelu_elementwise,
     pin_small_exact_integers,
 ]

@@ -33,7 +33,9 @@ MUTATIONS = {
     "gelu_cubic_decimal_slip": ("0.7978845608 * (x + 0.044715", "0.7978845608 * (x + 0.44715"),
     "gelu_two_over_pi": ("0.7978845608 * (x + 0.044715", "0.6366197724 * (x + 0.044715"),
     "gelu_dropped_cubic": ("(x + 0.044715 * x * x * x)", "(x)"),
-    "gelu_sign": ("(1.0 + tanh(", "(1.0 - tanh("),
+    "gelu_exp_sign": ("(1.0 + exp(-2.0 * u))", "(1.0 + exp(2.0 * u))"),
+    "gelu_half_dropped": ("return 0.5 * x * (2.0 /", "return x * (2.0 /"),
+    "gelu_exp_of_u": ("exp(-2.0 * u)", "exp(-u)"),
     "epilogue_skipped": ("c[j] = oracle_gelu_tanh(c[j]);", "c[j] = c[j];"),
     "relu_as_abs": ("return x > 0.0 ? x : 0.0;", "return fabs(x);"),
     "relu_keeps_negatives": ("return x > 0.0 ? x : 0.0;", "return x < 0.0 ? x : 0.0;"),
