@@ -1,4 +1,5 @@
-"""Python binding of the MI355X software-pipelined tiled GEMM (C ABI in include/spgemm.h).
+"""Python binding of the MI355X software-pipelined tiled GEMM (C ABI in include/spgemm.h)
+and of the standalone elementwise GELU (include/spgelu.h).
 
 Argument marshalling only: every step of C = epi(A . B) runs in the HIP
 kernels of ``libspgemm.so``.  PyTorch is used by callers for device memory and
@@ -65,7 +66,7 @@ class TileConfig(ctypes.Structure):
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_get_config", "gemm_autotune",
             "gemm_num_configs", "gemm_list_config", "gemm_lds_bytes", "gemm_status_string",
-            "gemm_last_hip_error")
+            "gemm_last_hip_error", "gelu_run")
 
 _lib = None
 
@@ -107,6 +108,8 @@ def lib():
     L.gemm_status_string.argtypes = [ctypes.c_int]
     L.gemm_last_hip_error.restype = ctypes.c_char_p
     L.gemm_last_hip_error.argtypes = []
+    L.gelu_run.restype = ctypes.c_int
+    L.gelu_run.argtypes = [vp, vp, i64, ctypes.c_int, vp]
     _lib = L
     return L
 
@@ -192,6 +195,12 @@ def gemm_status_string(status: int) -> str:
 
 def gemm_last_hip_error() -> str:
     return lib().gemm_last_hip_error().decode()
+
+
+def gelu_run(x, y, n: int, dtype: str = "bf16", stream=None) -> None:
+    """y[i] = gelu(x[i]) for n contiguous elements of dtype (include/spgelu.h)."""
+    st = lib().gelu_run(_ptr(x), _ptr(y), n, DTYPES[dtype], _stream(stream, x, y))
+    _check(st, "gelu_run")
 
 
 class Gemm:

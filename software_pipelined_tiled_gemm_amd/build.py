@@ -1,7 +1,8 @@
 """Build libspgemm.so (the HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
 The kernel instantiations are spread over csrc/gemm_tu*.hip so that they compile
-in parallel; csrc/gemm.hip holds the host side (C ABI, variant table).
+in parallel; csrc/gemm.hip holds the GEMM's host side (C ABI, variant table) and
+csrc/gelu.hip the standalone elementwise GELU (include/spgelu.h).
 """
 
 from __future__ import annotations
@@ -33,7 +34,8 @@ def _jobs() -> int:
 
 
 def build(out: str = OUT, extra=()) -> str:
-    sources = [os.path.join(CSRC, "gemm.hip")] + sorted(glob.glob(os.path.join(CSRC, "gemm_tu*.hip")))
+    sources = ([os.path.join(CSRC, "gemm.hip"), os.path.join(CSRC, "gelu.hip")]
+               + sorted(glob.glob(os.path.join(CSRC, "gemm_tu*.hip"))))
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     with tempfile.TemporaryDirectory(prefix="spgemm_build_") as tmp:
         def compile_one(src):

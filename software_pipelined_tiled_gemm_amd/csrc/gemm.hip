@@ -19,8 +19,25 @@
 #include <tuple>
 #include <vector>
 
+#include "errors.hpp"
 #include "launch.hpp"
 
+namespace spg {
+
+namespace {
+thread_local char g_last_hip_error[256] = "";
+}  // namespace
+
+gemm_status hip_fail(hipError_t e) {
+    snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s (%d)", hipGetErrorString(e), (int)e);
+    return GEMM_ERR_HIP;
+}
+
+const char* last_hip_error() { return g_last_hip_error; }
+
+}  // namespace spg
+
+using spg::hip_fail;
 using spg::KArgs;
 using spg::launch_fn;
 using spg::launch_pipelined;
@@ -58,13 +75,6 @@ struct ProblemKey {
         return std::tie(M, N, K, in, out, bl, epi) < std::tie(o.M, o.N, o.K, o.in, o.out, o.bl, o.epi);
     }
 };
-
-thread_local char g_last_hip_error[256] = "";
-
-gemm_status hip_fail(hipError_t e) {
-    snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s (%d)", hipGetErrorString(e), (int)e);
-    return GEMM_ERR_HIP;
-}
 
 std::mutex g_tuned_mu;
 std::map<ProblemKey, gemm_tile_config> g_tuned;
@@ -205,7 +215,7 @@ const char* gemm_status_string(gemm_status s) {
     return "unknown status";
 }
 
-const char* gemm_last_hip_error(void) { return g_last_hip_error; }
+const char* gemm_last_hip_error(void) { return spg::last_hip_error(); }
 
 int32_t gemm_num_configs(void) { return kNumVariants; }
 

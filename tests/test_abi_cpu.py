@@ -3,6 +3,7 @@ symbol, validates arguments before any HIP call, and its host-side planning logi
 (configuration table, LDS budget, heuristic) behaves as documented.  No kernel runs."""
 
 import ctypes
+import glob
 import os
 import re
 
@@ -11,7 +12,7 @@ import pytest
 import software_pipelined_tiled_gemm_amd as spg
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "spgemm.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("spgemm.h", "spgelu.h")]
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 
@@ -23,9 +24,15 @@ def L():
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(gemm_[a-z_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b((?:gemm|gelu)_[a-z_]+)\s*\(", src))
+    return sorted(names)
+
+
+def test_every_header_is_listed():
+    assert sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))) == sorted(HEADERS)
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -53,6 +60,13 @@ def test_invalid_arguments_rejected_without_gpu(L):
     assert ok(8, 8, 8, 0, 0, 2, 0) == 1    # unknown layout
     assert ok(8, 8, 8, 0, 0, 0, 5) == 1    # unknown epilogue
     assert ok(1 << 40, 8, 8, 0, 0, 0, 0) == 2
+    # the standalone GELU: n < 0, unknown dtype, NULL with n > 0; n == 0 is a no-op
+    assert L.gelu_run(None, None, -1, 1, None) == 1
+    assert L.gelu_run(None, None, 8, 5, None) == 1
+    assert L.gelu_run(None, None, 8, 1, None) == 1
+    assert L.gelu_run(None, None, 0, 1, None) == 0
+    assert L.gelu_run(None, None, 1 << 40, 1, None) == 1
+    assert L.gelu_run(16, 32, 1 << 40, 1, None) == 2    # over the grid limit: no launch
     # NULL handle / pointers
     assert L.gemm_run(None, None, None, None, None) == 1
     assert L.gemm_get_config(None, None) == 1
