@@ -65,6 +65,58 @@ def time_gemm(w, steps, warmup, force=None):
     return wall_ms, kern_ms, cfg
 
 
+def time_gelu(n, dtype, steps, warmup):
+    """Mean kernel time (ms) of the standalone GELU over n resident elements."""
+    import numpy as np
+    import torch
+
+    import software_pipelined_tiled_gemm_amd as spg
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    x = W.make_matrix((n,), dtype, ("normal", 1.0), W.SEED_A)
+    X = torch.from_numpy(x.view(np.int16)).to(dev)
+    Y = torch.empty_like(X)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        spg.gelu_run(X, Y, n, dtype, stream)
+    torch.cuda.synchronize(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        spg.gelu_run(X, Y, n, dtype, stream)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    return e0.elapsed_time(e1) / steps
+
+
+def gelu_lines(steps, warmup):
+    """The standalone GELU on the XLA page's bf16 [6,512,4096] tensor (HBM roofline), and
+    the GELU'd GEMM of that shape fused (epilogue) against unfused (GEMM, then GELU)."""
+    import workloads as W
+
+    n = 6 * 512 * 4096
+    ms = time_gelu(n, "bf16", steps, warmup)
+    gbs = 2 * n * 2 / (ms * 1e-3) / 1e9
+    out = {"gelu_bf16_6x512x4096": {
+        "kernel_us": round(ms * 1e3, 2), "GB_per_s": round(gbs, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": 4 * n}}}
+    wf = W.WORKLOADS["nn_bf16_3072x4096x4096_gelu"]
+    wp = W.custom(wf.M, wf.N, wf.K, wf.in_dtype, wf.out_dtype, wf.b_layout, "none", wf.dist,
+                  name="nn_bf16_3072x4096x4096")
+    _, k_fused, _ = time_gemm(wf, steps, warmup)
+    _, k_plain, _ = time_gemm(wp, steps, warmup)
+    k_gelu = time_gelu(wf.M * wf.N, "bf16", steps, warmup)
+    out["gemm_gelu_3072x4096x4096"] = {
+        "fused_us": round(k_fused * 1e3, 2), "gemm_us": round(k_plain * 1e3, 2),
+        "gelu_us": round(k_gelu * 1e3, 2), "unfused_us": round((k_plain + k_gelu) * 1e3, 2),
+        "fused_tflops": round(wf.flops / (k_fused * 1e-3) / 1e12, 2)}
+    return out
+
+
 def sustained_clock(w, seconds=2.0):
     """Runs the workload back to back for `seconds` while sampling the engine clock the
     SMU reports (rocm-smi); returns (median MHz, kernel us at that time) or None."""
@@ -229,7 +281,8 @@ def main():
                     help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging[:WMxWN[:lookahead]]]]] "
                          "(default: the library's choice)")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the extra lines (fp16 8192^3, the 8-GPU shard, the sustained clock)")
+                    help="skip the extra lines (fp16 8192^3, the 8-GPU shard, the standalone "
+                         "GELU, fused vs unfused GELU GEMM, the sustained clock)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy 5 times, so that HBM "
                          "byte counters can be scaled against a kernel of known traffic")
@@ -271,6 +324,9 @@ def main():
                            "tflops": round(wsh.flops / (ksh * 1e-3) / 1e12, 2),
                            "kernel_us": round(ksh * 1e3, 2), "config": cfgsh.as_dict()}
         log(f"  shard of 8: {extra[wsh.name]}")
+        extra.update(gelu_lines(args.steps, min(args.warmup, 200)))
+        log(f"  gelu: {extra['gelu_bf16_6x512x4096']}")
+        log(f"  fused vs unfused GELU GEMM: {extra['gemm_gelu_3072x4096x4096']}")
         clk = sustained_clock(w)
         if clk is not None:
             mhz, us = clk

@@ -45,10 +45,16 @@ __device__ __forceinline__ void store_elem(void* p, int64_t i, float v) {
 template <int DT>
 __device__ __forceinline__ u32x4 gelu_vec(u32x4 v) {
     if constexpr (DT == GEMM_F32) {
+        // each element goes through a scalar first: a bit cast applied directly to an
+        // element of a vector value read element 0 whatever the index (seen with this
+        // toolchain: 4 of 16 exponentials left in the kernel)
+        u32x4 r;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            v[e] = __builtin_bit_cast(uint32_t, gelu_tanh(__builtin_bit_cast(float, v[e])));
-        return v;
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t b = v[e];
+            r[e] = __builtin_bit_cast(uint32_t, gelu_tanh(__builtin_bit_cast(float, b)));
+        }
+        return r;
     } else {
         constexpr bool BF = DT == GEMM_BF16;
         u32x4 r;
