@@ -91,6 +91,27 @@ def time_gelu(n, dtype, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def copy_rate(nbytes, steps, warmup):
+    """GB/s (read + write) of a plain device-to-device copy of nbytes: what the memory
+    system gives a streaming kernel of that size, beside the 8 TB/s published peak."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(warmup):
+        b.copy_(a)
+    torch.cuda.synchronize(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize(dev)
+    return 2 * nbytes / (e0.elapsed_time(e1) / steps * 1e-3) / 1e9
+
+
 def gelu_lines(steps, warmup):
     """The standalone GELU on the XLA page's bf16 [6,512,4096] tensor (HBM roofline), and
     the GELU'd GEMM of that shape fused (epilogue) against unfused (GEMM, then GELU)."""
@@ -99,8 +120,10 @@ def gelu_lines(steps, warmup):
     n = 6 * 512 * 4096
     ms = time_gelu(n, "bf16", steps, warmup)
     gbs = 2 * n * 2 / (ms * 1e-3) / 1e9
+    copy_gbs = copy_rate(2 * n, steps, warmup)
     out = {"gelu_bf16_6x512x4096": {
         "kernel_us": round(ms * 1e3, 2), "GB_per_s": round(gbs, 1),
+        "device_copy_same_bytes_GB_per_s": round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes": 4 * n}}}

@@ -8,10 +8,10 @@
 // design is about bytes in flight, not arithmetic:
 //  * 16 bytes per lane per access (8 fp16/bf16 or 4 fp32 elements), 64 lanes of
 //    a wave covering 1 KiB of consecutive bytes;
-//  * UNROLL independent 16-byte loads per lane issued before any use, so each
-//    wave keeps 4 KiB of reads in flight;
-//  * one workgroup per 256 * UNROLL vectors, i.e. thousands of workgroups for
-//    the [6,512,4096] tensor, spread over all 256 CUs;
+//  * one 16-byte vector per lane and one workgroup per 256 vectors: 6144
+//    workgroups for the [6,512,4096] tensor, ~24 per CU, so every CU keeps many
+//    waves' reads in flight (2, 4, 8 or 16 vectors per lane measured 3-30%
+//    slower: fewer workgroups, later first stores);
 //  * loads and stores marked nontemporal: the data is touched once.
 // The arithmetic is the GEMM epilogue's (gelu_tanh in gemm_kernels.hpp): fp32,
 // then round-to-nearest-even into the element type.
@@ -27,7 +27,7 @@ namespace spg {
 namespace {
 
 constexpr int kGeluThreads = 256;
-constexpr int kGeluUnroll = 4;
+constexpr int kGeluUnroll = 1;   // measured best: more per lane only cuts the workgroup count
 
 template <int DT>
 __device__ __forceinline__ float load_elem(const void* p, int64_t i) {
