@@ -76,7 +76,11 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1, GEMM_EPI_RELU = 2 } ge
  *                       (buffer_load ... lds), a k-tile's copies issued together;
  *                       1 = copied into VGPRs one k-tile ahead and written to LDS
  *                       with ds_write_b128; 2 = straight into LDS, the copies of a
- *                       k-tile spread evenly between two barriers (stages >= 3)
+ *                       k-tile spread evenly between two barriers (stages >= 3);
+ *                       3 = wave-specialized (the Pallas guide's warp-specialized
+ *                       pipeline): one producer wave issues every copy, the
+ *                       consumer waves only read LDS and multiply, and per-slot
+ *                       counters in LDS replace the barrier
  *   lookahead           MFMA k-steps between the LDS read of an operand fragment and
  *                       its use: 1 (two fragment sets in registers) or 2 (four sets;
  *                       block_k 64, stages >= 2)

@@ -250,7 +250,7 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
             force->stages <= 0 || force->wave_m <= 0 || force->wave_n <= 0 ||
             force->group_m < 0 || (force->swizzle != 0 && force->swizzle != 1) ||
             (force->xcd_remap != 0 && force->xcd_remap != 1) ||
-            force->staging < 0 || force->staging > 2 ||
+            force->staging < 0 || force->staging > 3 ||
             (force->lookahead != 1 && force->lookahead != 2))
             return GEMM_ERR_INVALID_ARG;
         if (gemm_lds_bytes(force) > 160 * 1024) return GEMM_ERR_UNSUPPORTED;

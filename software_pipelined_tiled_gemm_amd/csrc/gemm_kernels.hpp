@@ -832,6 +832,258 @@ pipelined_gemm(KArgs args) {
 }
 
 // ---------------------------------------------------------------------------
+// wave-specialized variant: one producer wave, NC consumer waves
+// ---------------------------------------------------------------------------
+//
+// The warp-specialized pipeline of the Mosaic GPU pipelining guide (its "warp
+// specialization" section and second matmul example): one wave issues every
+// copy of the ring, the other waves only read LDS and run MFMA, and per-slot
+// counters in LDS take the place of the per-k-tile workgroup barrier:
+//   full[s]  = 1 + the last k-tile whose copies into slot s have completed
+//              (written by the producer after s_waitcnt vmcnt, release store);
+//   freed[s] = how many times a consumer wave has finished reading slot s
+//              (each consumer adds 1 after its last read of a k-tile, release).
+// Consumers wait for full[t % S] >= t + 1 before reading k-tile t; the producer
+// waits for freed[s] >= NC * (t / S) before copying k-tile t into slot s.
+// Every wait is bounded (kSpinMax polls with s_sleep in between, ~0.1 s): if a
+// counter never arrived the wave goes on with wrong data instead of hanging.
+// The register file allots every wave of a workgroup the same VGPRs, so the
+// producer costs a consumer's worth of registers: with 128x64 consumer tiles
+// (two waves per SIMD at most) the tile is 256x128, four consumers + one producer.
+constexpr int kSpinMax = 1 << 21;
+
+// Ordering is explicit rather than through acquire/release atomics (whose
+// workgroup-scope lowering may wait for every outstanding copy): the producer
+// waits with s_waitcnt vmcnt for the copies a counter announces before it
+// stores the counter; a consumer waits with s_waitcnt lgkmcnt(0) for its reads
+// before it adds to one.  The LDS executes one wave's operations in order, so
+// reads issued after a counter load has returned see what the counter announced;
+// the compiler fence keeps them after the loop.
+__device__ __forceinline__ void wait_at_least(uint32_t* p, uint32_t target) {
+    for (int it = 0; it < kSpinMax; ++it) {
+        if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    asm volatile("" ::: "memory");
+}
+
+template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S>
+struct WsGeom {
+    static constexpr int WAVES_N = BN / WN;
+    static constexpr int NC = (BM / WM) * WAVES_N;     // consumer waves
+    static constexpr int NT = (NC + 1) * 64;           // + the producer wave
+    static constexpr int TM = WM / 32, TN = WN / 32;
+    static constexpr int KSTEPS = BK / 16;
+    static constexpr int ROWB = BK * 2;
+    static constexpr int A_BYTES = BM * BK * 2;
+    static constexpr int STAGE = A_BYTES + BN * BK * 2;
+    static constexpr int A_OPS = A_BYTES / 1024;       // copy instructions of one k-tile
+    static constexpr int L = STAGE / 1024;
+    static constexpr int STG = 32 * WN * 4;
+    static_assert(BK == 64, "k-tile of 64");
+    static_assert(S >= 2 && S * STAGE <= 160 * 1024 - 64, "LDS budget");
+    static_assert(L < 64, "vmcnt range");
+    static_assert(NC * STG <= S * STAGE, "epilogue staging must fit the ring");
+    static_assert(BN >= 128, "[K,N] swizzle needs 16 chunks per row");
+};
+
+template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S>
+__global__ void __launch_bounds__((WsGeom<BF16, B_NK, BM, BN, BK, WM, WN, S>::NT))
+ws_gemm(KArgs args) {
+    using G = WsGeom<BF16, B_NK, BM, BN, BK, WM, WN, S>;
+    constexpr int NC = G::NC, TM = G::TM, TN = G::TN, ROWB = G::ROWB, A_BYTES = G::A_BYTES;
+    constexpr int L = G::L, A_OPS = G::A_OPS;
+    constexpr int CPR_K = BK / 8, RPI_K = 64 / CPR_K;
+
+    __shared__ __attribute__((aligned(1024))) char ring[S * G::STAGE];
+    __shared__ uint32_t full[S];
+    __shared__ uint32_t freed[S];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int tm, tn;
+    tile_of(blockIdx.x, args, tm, tn);
+    const int M = args.M, N = args.N, K = args.K;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nk = (K + BK - 1) / BK;
+    const int pad = (BK - K % BK) % BK;
+
+    if (threadIdx.x < S) { full[threadIdx.x] = 0; freed[threadIdx.x] = 0; }
+    __syncthreads();
+
+    SPG_LDS char* ring_l = (SPG_LDS char*)ring;
+    auto slot = [&](int t) __attribute__((always_inline)) { return ring_l + (t % S) * G::STAGE; };
+
+    floatx16 acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
+
+    if (wave == NC) {
+        // ---- producer: every copy of the ring --------------------------------------
+        const int a_rows = (M - m0) < BM ? (M - m0) : BM;
+        const uint64_t a_base = (uint64_t)(uintptr_t)(args.A + (size_t)m0 * K);
+        const uint32_t a_bytes = (uint32_t)a_rows * (uint32_t)K * 2u;
+        uint64_t b_base;
+        uint32_t b_bytes, b_kb;
+        if constexpr (B_NK) {
+            const int b_rows = (N - n0) < BN ? (N - n0) : BN;
+            b_base = (uint64_t)(uintptr_t)(args.B + (size_t)n0 * K);
+            b_bytes = (uint32_t)b_rows * (uint32_t)K * 2u;
+            b_kb = 2u;
+        } else {
+            b_base = (uint64_t)(uintptr_t)(args.B + n0);
+            b_bytes = (uint32_t)(((size_t)K * N - n0) * 2u);
+            b_kb = 2u * (uint32_t)N;
+        }
+        auto rsrc = [&](uint64_t base, uint32_t bytes, uint32_t kb, int kt) {
+            const int64_t shift = (int64_t)(kt * BK - pad) * (int64_t)kb;
+            return make_rsrc((const void*)(uintptr_t)(base + (uint64_t)shift), bytes - (uint32_t)shift);
+        };
+        // per-lane offsets of copy op j (the same layout the pipelined kernel uses)
+        uint32_t off[L];
+        int kin[L];
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            if (j < A_OPS || B_NK) {
+                const int d = j < A_OPS ? j : j - A_OPS;
+                const int r = d * RPI_K + lane / CPR_K;
+                const int p = lane % CPR_K;
+                const int c = p ^ kswz_t<BK>(r);
+                off[j] = (uint32_t)r * (uint32_t)K * 2u + (uint32_t)c * 16u;
+                kin[j] = c * 8;
+            } else {
+                constexpr int CPR = BN / 8, RP = 64 / CPR;
+                const int d = j - A_OPS;
+                const int r = d * RP + lane / CPR;
+                const int p = lane % CPR;
+                const int c = p ^ nswz(r);
+                off[j] = n0 + c * 8 + 8 > N ? kOOB : (uint32_t)r * (uint32_t)N * 2u + (uint32_t)c * 16u;
+                kin[j] = r;
+            }
+        }
+        auto issue = [&](int t, bool first) __attribute__((always_inline)) {
+            const i32x4 ra = rsrc(a_base, a_bytes, 2u, t), rb = rsrc(b_base, b_bytes, b_kb, t);
+            SPG_LDS char* dst = slot(t);
+#pragma unroll
+            for (int j = 0; j < L; ++j) {
+                const uint32_t o = first && kin[j] < pad ? kOOB : off[j];
+                dma16(j < A_OPS ? ra : rb, dst + j * 1024, o);
+            }
+        };
+        auto publish = [&](int t) __attribute__((always_inline)) {
+            asm volatile("" ::: "memory");
+            if (lane == 0)
+                __hip_atomic_store(&full[t % S], (uint32_t)(t + 1), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+        };
+        issue(0, true);
+        for (int t = 1; t < nk; ++t) {
+            if (t >= S) wait_at_least(&freed[t % S], (uint32_t)(NC * (t / S)));
+            issue(t, false);
+            wait_vmcnt<L>();      // k-tile t-1 has landed
+            publish(t - 1);
+        }
+        wait_vmcnt<0>();
+        publish(nk - 1);
+    } else {
+        // ---- consumers: LDS reads and MFMA only ---------------------------------------
+        int aoff[G::KSTEPS];
+#pragma unroll
+        for (int kk = 0; kk < G::KSTEPS; ++kk) {
+            const int c = kk * 2 + (lane >> 5), r = lane & 31;
+            aoff[kk] = (wm * WM + r) * ROWB + (c ^ kswz_t<BK>(r)) * 16;
+        }
+        int boff[B_NK ? G::KSTEPS : TN];
+        if constexpr (B_NK) {
+#pragma unroll
+            for (int kk = 0; kk < G::KSTEPS; ++kk) {
+                const int c = kk * 2 + (lane >> 5), r = lane & 31;
+                boff[kk] = A_BYTES + (wn * WN + r) * ROWB + (c ^ kswz_t<BK>(r)) * 16;
+            }
+        } else {
+            constexpr int RB = BN * 2;
+            const int kl = (lane >> 5) * 8 + ((lane & 15) >> 2);
+#pragma unroll
+            for (int bn = 0; bn < TN; ++bn) {
+                const int chunk = (wn * WN + bn * 32) / 8 + ((lane >> 4) & 1) * 2 + ((lane >> 1) & 1);
+                boff[bn] = A_BYTES + kl * RB + (chunk ^ nswz(kl)) * 16 + (lane & 1) * 8;
+            }
+        }
+        struct Frags { u32x4 a[TM]; u32x4 b[TN]; };
+        constexpr int NRD = TM + (B_NK ? TN : 2 * TN);
+        auto read_op = [&](const SPG_LDS char* sl, int kk, Frags& f, auto rc) __attribute__((always_inline)) {
+            constexpr int r = decltype(rc)::value;
+            if constexpr (r < TM) {
+                f.a[r] = *(const SPG_LDS u32x4*)(sl + aoff[kk] + r * 32 * ROWB);
+            } else if constexpr (B_NK) {
+                f.b[r - TM] = *(const SPG_LDS u32x4*)(sl + boff[kk] + (r - TM) * 32 * ROWB);
+            } else {
+                constexpr int bn = (r - TM) / 2, h = (r - TM) % 2, RB = BN * 2;
+                const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (SPG_LDS shortx4*)(sl + boff[bn] + (kk * 16 + h * 4) * RB));
+                const u32x2 v2 = __builtin_bit_cast(u32x2, v);
+                f.b[bn][2 * h] = v2[0];
+                f.b[bn][2 * h + 1] = v2[1];
+            }
+        };
+        // one MFMA stage of `now` with the reads of the next stage spread over its steps
+        auto stage = [&](const Frags& now, const SPG_LDS char* sl, int kk, Frags& nx) __attribute__((always_inline)) {
+            constexpr int NMMA = TN * TM, RPS = 2;
+            constexpr int STEPS = NMMA > (NRD + 1) / RPS ? NMMA : (NRD + 1) / RPS;
+            static_for<0, STEPS>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                if constexpr (i < NMMA)
+                    acc[i / TM][i % TM] = mfma<BF16>(now.b[i / TM], now.a[i % TM], acc[i / TM][i % TM]);
+                static_for<0, RPS>([&](auto rc) {
+                    constexpr int r = i * RPS + decltype(rc)::value;
+                    if constexpr (r < NRD) read_op(sl, kk, nx, std::integral_constant<int, r>{});
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        Frags f0, f1;
+        wait_at_least(&full[0], 1u);
+        static_for<0, NRD>([&](auto rc) { read_op(slot(0), 0, f0, rc); });
+        for (int t = 0; t < nk; ++t) {
+            const SPG_LDS char* cur = slot(t);
+            stage(f0, cur, 1, f1);
+            stage(f1, cur, 2, f0);
+            stage(f0, cur, 3, f1);
+            // this wave's reads of slot t % S are all issued: once they have returned
+            // the slot is free for the producer
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (lane == 0)
+                __hip_atomic_fetch_add(&freed[t % S], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (t + 1 < nk) wait_at_least(&full[(t + 1) % S], (uint32_t)(t + 2));
+            // reads the first step of k-tile t+1 (a stale slot after the last one: unused)
+            stage(f1, slot(t + 1), 0, f0);
+        }
+    }
+
+    // ---- epilogue (consumers), staging in the drained ring ----------------------------
+    __syncthreads();
+    if (wave < NC) {
+        char* stg = ring + wave * G::STG;
+        const int m_base = m0 + wm * WM, n_base = n0 + wn * WN;
+        const int od = args.out_dtype, ep = args.epilogue;
+        auto store_as = [&](auto odc) __attribute__((always_inline)) {
+            constexpr int OD = decltype(odc)::value;
+            if (ep == kEpiGelu) store_tile<OD, kEpiGelu, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+            else if (ep == kEpiRelu) store_tile<OD, kEpiRelu, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+            else store_tile<OD, kEpiNone, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+        };
+        if (od == kOutF32) store_as(std::integral_constant<int, kOutF32>{});
+        else if (od == kOutBF16) store_as(std::integral_constant<int, kOutBF16>{});
+        else store_as(std::integral_constant<int, kOutF16>{});
+    }
+}
+
+// ---------------------------------------------------------------------------
 // simple kernel: any shape, any alignment, any K (including 0)
 // ---------------------------------------------------------------------------
 

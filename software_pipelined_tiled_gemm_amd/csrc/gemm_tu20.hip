@@ -25,4 +25,5 @@
 #define SPG_V_18(...)
 #define SPG_V_19(...)
 #define SPG_V_20(...) SPG_INSTANTIATE_ALL(__VA_ARGS__)
+#define SPG_V_21(...)
 #include "variants.inc"

@@ -18,9 +18,15 @@ void launch_pipelined(const KArgs& a, dim3 grid, hipStream_t st);
 template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ, int LDM,
           int PF>
 void launch_pipelined(const KArgs& a, dim3 grid, hipStream_t st) {
-    using G = Geom<BM, BN, BK, WM, WN, S>;
-    hipLaunchKernelGGL((pipelined_gemm<BF16, B_NK, BM, BN, BK, WM, WN, S, SWZ, LDM, PF>), grid,
-                       dim3(G::NT), 0, st, a);
+    if constexpr (LDM == 3) {
+        // a producer wave and consumer waves (wave-specialized ring)
+        using W = WsGeom<BF16, B_NK, BM, BN, BK, WM, WN, S>;
+        hipLaunchKernelGGL((ws_gemm<BF16, B_NK, BM, BN, BK, WM, WN, S>), grid, dim3(W::NT), 0, st, a);
+    } else {
+        using G = Geom<BM, BN, BK, WM, WN, S>;
+        hipLaunchKernelGGL((pipelined_gemm<BF16, B_NK, BM, BN, BK, WM, WN, S, SWZ, LDM, PF>), grid,
+                           dim3(G::NT), 0, st, a);
+    }
 }
 #endif
 
