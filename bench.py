@@ -263,7 +263,7 @@ def measured_traffic(workload: str, forced: bool):
 
 
 def parse_tile(spec):
-    """'256x256x64:2[:swizzle[:group_m[:staging[:WMxWN[:lookahead]]]]]' -> the matching
+    """'256x256x64:2[:swizzle[:group_m[:staging[:WMxWN[:lookahead[:schedule]]]]]]' -> the matching
     compiled configuration (the first one in the table when the wave tile is not given)."""
     import software_pipelined_tiled_gemm_amd as spg
 
@@ -277,11 +277,12 @@ def parse_tile(spec):
     stg = int(parts[4]) if len(parts) > 4 else 0
     wave = tuple(int(x) for x in parts[5].lower().split("x")) if len(parts) > 5 else None
     look = int(parts[6]) if len(parts) > 6 else 1
+    sched = int(parts[7]) if len(parts) > 7 else 0
     for i in range(spg.gemm_num_configs()):
         c = spg.gemm_list_config(i)
         if wave is not None and (c.wave_m, c.wave_n) != wave:
             continue
-        if c.lookahead != look:
+        if c.lookahead != look or c.schedule != sched:
             continue
         if (c.block_m, c.block_n, c.block_k, c.stages, c.swizzle, c.staging) == (bm, bn, bk, st, swz, stg):
             if gm:
@@ -301,7 +302,7 @@ def main():
     ap.add_argument("--workload", default="nn_bf16_8192",
                     help="workload name from workloads.WORKLOADS")
     ap.add_argument("--tile", default=None,
-                    help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging[:WMxWN[:lookahead]]]]] "
+                    help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging[:WMxWN[:lookahead[:schedule]]]]]] "
                          "(default: the library's choice)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra lines (fp16 8192^3, the 8-GPU shard, the standalone "

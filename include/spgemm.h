@@ -84,6 +84,10 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1, GEMM_EPI_RELU = 2 } ge
  *   lookahead           MFMA k-steps between the LDS read of an operand fragment and
  *                       its use: 1 (two fragment sets in registers) or 2 (four sets;
  *                       block_k 64, stages >= 2)
+ *   schedule            0 = instructions of a stage placed by hand (each MFMA step
+ *                       followed by its copy op and LDS reads, the TileLang
+ *                       tutorial's manual stage/order placement); 1 = the same
+ *                       instructions placed by the compiler (its planned pipeline)
  * The LDS a configuration needs is stages * (block_m + block_n) * block_k * 2 bytes
  * (the shared-memory bound of the TileLang tutorial's shared_bytes()), at most 160 KiB. */
 typedef struct {
@@ -95,6 +99,7 @@ typedef struct {
     int32_t xcd_remap;
     int32_t staging;
     int32_t lookahead;
+    int32_t schedule;
 } gemm_tile_config;
 
 typedef struct gemm_plan* gemm_handle;

@@ -40,7 +40,7 @@ class TileConfig(ctypes.Structure):
                 ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32),
                 ("swizzle", ctypes.c_int32), ("group_m", ctypes.c_int32),
                 ("xcd_remap", ctypes.c_int32), ("staging", ctypes.c_int32),
-                ("lookahead", ctypes.c_int32)]
+                ("lookahead", ctypes.c_int32), ("schedule", ctypes.c_int32)]
 
     def __init__(self, **kw):
         kw.setdefault("lookahead", 1)
@@ -61,7 +61,8 @@ class TileConfig(ctypes.Structure):
         return (f"TileConfig({d['block_m']}x{d['block_n']}x{d['block_k']}, S={d['stages']}, "
                 f"wave {d['wave_m']}x{d['wave_n']}, swizzle={d['swizzle']}, "
                 f"group_m={d['group_m']}, xcd_remap={d['xcd_remap']}, "
-                f"staging={STAGING.get(d['staging'], d['staging'])}, lookahead={d['lookahead']})")
+                f"staging={STAGING.get(d['staging'], d['staging'])}, lookahead={d['lookahead']}, "
+                f"schedule={'compiler' if d['schedule'] else 'manual'})")
 
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_get_config", "gemm_autotune",

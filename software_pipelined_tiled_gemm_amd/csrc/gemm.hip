@@ -54,12 +54,12 @@ struct Variant {
     launch_fn fn[2][2];  // [bf16][b_nk]
 };
 
-#define SPG_V(unit, BM, BN, BK, WM, WN, S, SWZ, LDM, PF)                                   \
-    Variant{{BM, BN, BK, S, WM, WN, SWZ, 0, 1, LDM, PF},                                   \
-            {{launch_pipelined<false, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF>,  \
-              launch_pipelined<false, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF>},  \
-             {launch_pipelined<true, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF>,   \
-              launch_pipelined<true, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF>}}},
+#define SPG_V(unit, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED)                                    \
+    Variant{{BM, BN, BK, S, WM, WN, SWZ, 0, 1, LDM, PF, SCHED},                                    \
+            {{launch_pipelined<false, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF, SCHED>,   \
+              launch_pipelined<false, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF, SCHED>},   \
+             {launch_pipelined<true, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF, SCHED>,    \
+              launch_pipelined<true, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF, SCHED>}}},
 
 const Variant kVariants[] = {
 #include "variants.inc"
@@ -82,7 +82,8 @@ std::map<ProblemKey, gemm_tile_config> g_tuned;
 bool same_tile(const gemm_tile_config& a, const gemm_tile_config& b) {
     return a.block_m == b.block_m && a.block_n == b.block_n && a.block_k == b.block_k &&
            a.stages == b.stages && a.wave_m == b.wave_m && a.wave_n == b.wave_n &&
-           a.swizzle == b.swizzle && a.staging == b.staging && a.lookahead == b.lookahead;
+           a.swizzle == b.swizzle && a.staging == b.staging && a.lookahead == b.lookahead &&
+           a.schedule == b.schedule;
 }
 
 const Variant* find_variant(const gemm_tile_config& c) {
@@ -128,7 +129,8 @@ const Variant* find_cfg(int bm, int bn, int bk, int stages, int staging, int wm,
     for (const Variant& v : kVariants)
         if (v.cfg.block_m == bm && v.cfg.block_n == bn && v.cfg.block_k == bk &&
             v.cfg.stages == stages && v.cfg.staging == staging && v.cfg.swizzle == 1 &&
-            v.cfg.wave_m == wm && v.cfg.wave_n == wn && v.cfg.lookahead == lookahead)
+            v.cfg.wave_m == wm && v.cfg.wave_n == wn && v.cfg.lookahead == lookahead &&
+            v.cfg.schedule == 0)
             return &v;
     return nullptr;
 }
@@ -251,7 +253,8 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
             force->group_m < 0 || (force->swizzle != 0 && force->swizzle != 1) ||
             (force->xcd_remap != 0 && force->xcd_remap != 1) ||
             force->staging < 0 || force->staging > 3 ||
-            (force->lookahead != 1 && force->lookahead != 2))
+            (force->lookahead != 1 && force->lookahead != 2) ||
+            (force->schedule != 0 && force->schedule != 1))
             return GEMM_ERR_INVALID_ARG;
         if (gemm_lds_bytes(force) > 160 * 1024) return GEMM_ERR_UNSUPPORTED;
         var = find_variant(*force);

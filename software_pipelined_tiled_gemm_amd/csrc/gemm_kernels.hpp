@@ -345,8 +345,13 @@ __device__ __forceinline__ int kswz_t(int r) {
 // gives every read a whole extra stage to return, which a wave alone on its SIMD
 // needs when the LDS is busy.  The barrier of a k-tile sits PF stages before its
 // end, right after the last read of the slot.
+//
+// SCHED selects who places the instructions of a stage: 0 = by hand, every MFMA
+// step followed by its copy op and LDS reads and a scheduling barrier (the
+// TileLang tutorial's manual stage/order placement); 1 = the compiler, with the
+// same instructions and no scheduling barriers (its compiler-planned pipeline).
 template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ, int LDM,
-          int PF>
+          int PF, int SCHED>
 __global__ void __launch_bounds__((Geom<BM, BN, BK, WM, WN, S>::NT))
 pipelined_gemm(KArgs args) {
     using G = Geom<BM, BN, BK, WM, WN, S>;
@@ -603,7 +608,9 @@ pipelined_gemm(KArgs args) {
                 acc[bn][bm] = mfma<BF16>(f.b[bn], f.a[bm], acc[bn][bm]);
     };
     // keep each stage's loads and MFMAs together: no motion across stage boundaries
-    auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+    auto fence = []() __attribute__((always_inline)) {
+        if constexpr (SCHED == 0) __builtin_amdgcn_sched_barrier(0);
+    };
 
     constexpr int NMMA = TN * TM;
 #ifndef SPG_READS_PER_STEP

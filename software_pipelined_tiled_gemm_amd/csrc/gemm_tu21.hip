@@ -3,7 +3,7 @@
 #define SPG_DEFINE_LAUNCHERS
 #include "launch.hpp"
 
-#define SPG_V(unit, BM, BN, BK, WM, WN, S, SWZ, LDM, PF) SPG_V_##unit(BM, BN, BK, WM, WN, S, SWZ, LDM, PF)
+#define SPG_V(unit, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED) SPG_V_##unit(BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED)
 #define SPG_V_0(...)
 #define SPG_V_1(...)
 #define SPG_V_2(...)
@@ -26,4 +26,5 @@
 #define SPG_V_19(...)
 #define SPG_V_20(...)
 #define SPG_V_21(...) SPG_INSTANTIATE_ALL(__VA_ARGS__)
+#define SPG_V_22(...)
 #include "variants.inc"

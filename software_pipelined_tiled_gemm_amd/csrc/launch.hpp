@@ -11,12 +11,12 @@ namespace spg {
 typedef void (*launch_fn)(const KArgs&, dim3, hipStream_t);
 
 template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ, int LDM,
-          int PF>
+          int PF, int SCHED>
 void launch_pipelined(const KArgs& a, dim3 grid, hipStream_t st);
 
 #ifdef SPG_DEFINE_LAUNCHERS
 template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ, int LDM,
-          int PF>
+          int PF, int SCHED>
 void launch_pipelined(const KArgs& a, dim3 grid, hipStream_t st) {
     if constexpr (LDM == 3) {
         // a producer wave and consumer waves (wave-specialized ring)
@@ -24,7 +24,7 @@ void launch_pipelined(const KArgs& a, dim3 grid, hipStream_t st) {
         hipLaunchKernelGGL((ws_gemm<BF16, B_NK, BM, BN, BK, WM, WN, S>), grid, dim3(W::NT), 0, st, a);
     } else {
         using G = Geom<BM, BN, BK, WM, WN, S>;
-        hipLaunchKernelGGL((pipelined_gemm<BF16, B_NK, BM, BN, BK, WM, WN, S, SWZ, LDM, PF>), grid,
+        hipLaunchKernelGGL((pipelined_gemm<BF16, B_NK, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED>), grid,
                            dim3(G::NT), 0, st, a);
     }
 }
@@ -32,12 +32,12 @@ void launch_pipelined(const KArgs& a, dim3 grid, hipStream_t st) {
 
 }  // namespace spg
 
-#define SPG_INSTANTIATE_ALL(BM, BN, BK, WM, WN, S, SWZ, LDM, PF)                                        \
-    template void spg::launch_pipelined<false, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF>(     \
+#define SPG_INSTANTIATE_ALL(BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED)                                        \
+    template void spg::launch_pipelined<false, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF, SCHED>(     \
         const spg::KArgs&, dim3, hipStream_t);                                                     \
-    template void spg::launch_pipelined<false, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF>(      \
+    template void spg::launch_pipelined<false, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF, SCHED>(      \
         const spg::KArgs&, dim3, hipStream_t);                                                     \
-    template void spg::launch_pipelined<true, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF>(      \
+    template void spg::launch_pipelined<true, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF, SCHED>(      \
         const spg::KArgs&, dim3, hipStream_t);                                                     \
-    template void spg::launch_pipelined<true, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF>(       \
+    template void spg::launch_pipelined<true, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF, SCHED>(       \
         const spg::KArgs&, dim3, hipStream_t);
