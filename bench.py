@@ -291,6 +291,37 @@ def parse_tile(spec):
     raise SystemExit(f"no compiled configuration matches --tile {spec}")
 
 
+# Design-choice ablations at the headline workload: (label, --tile spec).  Each is a
+# distinct kernel instantiation, so a profiler run over `--ablations` attributes
+# counters to the rows by kernel name.
+ABLATIONS = [
+    ("default: 256x256x64, S=2, 8 waves of 128x64, direct copies", "256x256x64:2:1:8:0:128x64:1:0"),
+    ("no overlap (S=1, the serial loop), 4 waves", "256x256x64:1:1:8:0:128x128:1:0"),
+    ("4 waves of 128x128 (one per SIMD), lookahead 1", "256x256x64:2:1:8:0:128x128:1:0"),
+    ("4 waves of 128x128, lookahead 2", "256x256x64:2:1:8:0:128x128:2:0"),
+    ("register-staged copies (VGPR -> ds_write), 8 waves", "256x256x64:2:1:8:1:128x64:1:0"),
+    ("copies spread over the barrier window (BK=32, S=5), 8 waves", "256x256x32:5:1:8:2:128x64:1:0"),
+    ("compiler-placed schedule, 8 waves", "256x256x64:2:1:8:0:128x64:1:1"),
+    ("swizzled LDS, BK=32, S=4, 4 waves", "256x256x32:4:1:8:0:128x128:1:0"),
+    ("no swizzle, BK=32, S=4, 4 waves", "256x256x32:4:0:8:0:128x128:1:0"),
+    ("256x128 tile, 8 waves of 64x64, S=3", "256x128x64:3:1:8:0:64x64:1:0"),
+    ("256x128 tile, wave-specialized (producer wave + 4 consumers)", "256x128x64:3:1:8:3:128x64:1:0"),
+    ("128x128 tile, 4 waves of 64x64, S=3", "128x128x64:3:1:8:0:64x64:1:0"),
+]
+
+
+def run_ablations(w, steps, warmup):
+    rows = []
+    for label, spec in ABLATIONS:
+        cfg = parse_tile(spec)
+        _, k, used = time_gemm(w, steps, warmup, cfg)
+        rows.append({"label": label, "tile": spec, "kernel_us": round(k * 1e3, 2),
+                     "tflops": round(w.flops / (k * 1e-3) / 1e12, 2)})
+        log(f"  {label}: {rows[-1]['kernel_us']} us, {rows[-1]['tflops']} TFLOP/s")
+    print(json.dumps({"ablations": rows, "workload": w.name, "steps": steps, "warmup": warmup}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,6 +338,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra lines (fp16 8192^3, the 8-GPU shard, the standalone "
                          "GELU, fused vs unfused GELU GEMM, the sustained clock)")
+    ap.add_argument("--ablations", action="store_true",
+                    help="time the design-choice ablations (ABLATIONS) on the workload instead "
+                         "of the benchmark line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy 5 times, so that HBM "
                          "byte counters can be scaled against a kernel of known traffic")
@@ -326,6 +360,9 @@ def main():
 
     w = W.WORKLOADS[args.workload]
     log(f"bench: {w.describe()}")
+    if args.ablations:
+        run_ablations(w, args.steps, args.warmup)
+        return
     force = parse_tile(args.tile) if args.tile else None
     wall_ms, kern_ms, cfg = time_gemm(w, args.steps, args.warmup, force)
     tflops = w.flops / (kern_ms * 1e-3) / 1e12
