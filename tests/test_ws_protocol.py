@@ -74,7 +74,7 @@ def run_protocol(nk, S, NC, rng, short=0, max_steps=1_000_000):
         t = c["t"]
         if c["phase"] == "compute":               # reads of k-tile t (steps 1..3)
             assert t in landed, f"k-tile {t} read before its copies landed"
-            assert holder[t % S] == t
+            assert holder[t % S] == t, f"slot {t % S} refilled while k-tile {t} is read"
             c["phase"] = "release"
             return True
         if c["phase"] == "release":               # lgkmcnt(0), freed[t % S] += 1
@@ -86,7 +86,8 @@ def run_protocol(nk, S, NC, rng, short=0, max_steps=1_000_000):
             if full[(t + 1) % S] < t + 2:
                 return False
             reading[i] = t + 1                    # reads step 0 of k-tile t+1
-            assert (t + 1) in landed and holder[(t + 1) % S] == t + 1
+            assert (t + 1) in landed, f"k-tile {t + 1} read before its copies landed"
+            assert holder[(t + 1) % S] == t + 1, f"slot {(t + 1) % S} refilled while k-tile {t + 1} is read"
             c["t"] = t + 1
             c["phase"] = "compute"
             return True
