@@ -231,33 +231,41 @@ def cpu_baseline(w, target_s=15.0):
             "sample": f"{rows} of {w.M} rows of C (all {w.N} columns, K={w.K}), {dt:.1f} s"}
 
 
+KERNEL_SOURCE = os.path.join(ROOT, "software_pipelined_tiled_gemm_amd", "csrc", "gemm_kernels.hpp")
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the kernel sources (same recipe as the profile summaries record)."""
-    import glob
+    """sha256 of the device code (the same recipe the counter summaries record)."""
     import hashlib
 
-    h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "software_pipelined_tiled_gemm_amd", "csrc", "*"))):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
+    with open(KERNEL_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
 
 
-def measured_traffic(workload: str, forced: bool):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
-    or None when the kernel sources changed since the counters were taken (or the
-    configuration is not the default one they were taken on)."""
+def kernel_name(w, cfg) -> str:
+    """The template instantiation a configuration launches (as profilers print it)."""
+    b = lambda v: "true" if v else "false"
+    return (f"spg::pipelined_gemm<{b(w.in_dtype == 'bf16')}, {b(w.b_layout == 'nk')}, "
+            f"{cfg.block_m}, {cfg.block_n}, {cfg.block_k}, {cfg.wave_m}, {cfg.wave_n}, "
+            f"{cfg.stages}, {b(cfg.swizzle)}, {cfg.staging}, {cfg.lookahead}, {cfg.schedule}>")
+
+
+def measured_traffic(workload: str, cfg, w):
+    """HBM-side bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, or None unless it was taken on the same device code and the same kernel
+    instantiation this run launches."""
     path = os.path.join(ROOT, "profiles", f"pipelined_gemm_{workload}_counters.md")
-    if forced or not os.path.exists(path):
+    if not os.path.exists(path):
         return None
-    src, traffic = None, None
+    src, traffic, kern = None, None, None
     for line in open(path):
-        if "kernel sources sha256:" in line:
-            src = line.split(":", 1)[1].strip()
+        if "kernel sources sha256" in line:
+            src = line.rsplit(":", 1)[1].strip()
         if "traffic_bytes_per_launch:" in line:
             traffic = float(line.split(":", 1)[1].strip())
-    if src != kernel_source_hash():
+        if line.startswith("# kernel:"):
+            kern = line.split(":", 1)[1].strip()
+    if src != kernel_source_hash() or kern is None or kernel_name(w, cfg) not in kern:
         return None
     return traffic
 
@@ -430,7 +438,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": PEAK_TFLOPS[w.in_dtype], "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_TFLOPS[w.in_dtype], 4),
-                     "traffic": measured_traffic(w.name, force is not None),
+                     "traffic": measured_traffic(w.name, cfg, w),
                      "algorithmic_bytes": algo_bytes},
         "extra": extra,
     }

@@ -110,16 +110,19 @@ bool valid_dtype_in(int d) { return d == GEMM_F16 || d == GEMM_BF16; }
 bool valid_dtype_out(int d) { return d == GEMM_F16 || d == GEMM_BF16 || d == GEMM_F32; }
 
 // Shape conditions of the pipelined kernel: 16-B rows for the direct-to-LDS copies
-// and 32-bit buffer offsets.  Anything else runs on the simple kernel.
+// and 32-bit buffer offsets.  A copy resource spans at most 256 rows of A (or of a
+// [N,K] B) or all of a [K,N] B, plus up to 63 k of the leading partial k-tile; it
+// must stay within 2^31 bytes so that the out-of-range offset 2^31 reads zero.
+// Anything else runs on the simple kernel.
 bool pipelined_fits(int64_t M, int64_t N, int64_t K, gemm_b_layout bl) {
     if (K <= 0 || M <= 0 || N <= 0) return false;
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return false;
     if (K % 8 != 0) return false;
     const int64_t lim = (int64_t)1 << 31;
-    if (256 * K * 2 >= lim) return false;
+    if (256 * (K + 64) * 2 > lim) return false;
     if (bl == GEMM_B_KN) {
         if (N % 8 != 0) return false;
-        if (K * N * 2 >= lim) return false;
+        if ((K + 64) * N * 2 > lim) return false;
     }
     return true;
 }

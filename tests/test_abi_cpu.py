@@ -153,6 +153,25 @@ def test_unaligned_shapes_plan_the_simple_kernel(L):
     spg.gemm_destroy(h)
 
 
+def test_size_limits_of_the_pipelined_kernel(L):
+    # a copy resource (256 rows of A or of a [N,K] B, all of a [K,N] B, plus up to 63 k of
+    # the leading partial k-tile) must stay within 2^31 bytes: just inside runs pipelined,
+    # just outside plans the simple kernel (block_k = 0)
+    def bk(M, N, K, layout):
+        h = spg.gemm_create(M, N, K, "bf16", "bf16", layout)
+        c = spg.gemm_get_config(h).block_k
+        spg.gemm_destroy(h)
+        return c
+    kmax = (1 << 31) // (256 * 2) - 64          # 4,194,240
+    assert bk(40, 40, kmax, "nk") == 64
+    assert bk(40, 40, kmax + 8, "nk") == 0
+    K = 16376
+    nmax = ((1 << 31) // ((K + 64) * 2)) // 8 * 8   # 65,312
+    assert bk(48, nmax, K, "kn") == 64
+    assert bk(48, nmax + 8, K, "kn") == 0
+    assert bk(48, nmax + 8, K, "nk") == 64     # [N,K] B is bounded per 256-row panel
+
+
 def test_heuristic_tiles(L):
     def cfg(M, N, K):
         h = spg.gemm_create(M, N, K, "bf16", "bf16", "kn")

@@ -158,6 +158,27 @@ def test_deterministic_and_untouched_outside():
     assert torch.all(big[0] == 0x5A5A) and torch.all(big[-1] == 0x5A5A)
 
 
+@pytest.mark.parametrize("case", ["max_k_nk", "max_kn_bytes"])
+def test_largest_pipelined_operands(case):
+    # the largest operands the pipelined kernel takes (copy resources just inside 2^31
+    # bytes), with a leading partial k-tile (K % 64 = 56) and, for [K,N], a ragged N
+    # whose columns past N must read as zero
+    if case == "max_k_nk":
+        w = W.custom(40, 40, (1 << 31) // 512 - 72, W.BF16, W.BF16, W.B_NK)   # K = 4,194,232
+        rows = None
+    else:
+        K = 16376
+        N = ((1 << 31) // ((K + 64) * 2)) // 8 * 8                           # 65,312
+        w = W.custom(48, N, K, W.BF16, W.BF16, W.B_KN)
+        rows = np.array([0, 17, 47])
+    _log(f"{case}: {w.describe()}")
+    a, b = W.make_inputs(w)
+    C, cfg = G.run(w, a, b)
+    assert cfg.block_k == 64, cfg
+    res = G.check(w, a, b, G.c_values(C, w, rows), rows=rows)
+    _log(f"  err_q={res['err_q']:.3e}")
+
+
 def test_autotune_keeps_parity():
     w = W.custom(1024, 768, 512, W.F16, W.F16, W.B_NK)
     a, b = W.make_inputs(w)
