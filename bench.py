@@ -245,9 +245,13 @@ def kernel_source_hash() -> str:
 def kernel_name(w, cfg) -> str:
     """The template instantiation a configuration launches (as profilers print it)."""
     b = lambda v: "true" if v else "false"
+    # the persistent instantiation runs only on the shapes it takes (else its twin)
+    pers = (cfg.persistent and w.out_dtype != "f32" and w.K % cfg.block_k == 0
+            and (w.b_layout == "nk" or w.N % cfg.block_n == 0))
     return (f"spg::pipelined_gemm<{b(w.in_dtype == 'bf16')}, {b(w.b_layout == 'nk')}, "
             f"{cfg.block_m}, {cfg.block_n}, {cfg.block_k}, {cfg.wave_m}, {cfg.wave_n}, "
-            f"{cfg.stages}, {b(cfg.swizzle)}, {cfg.staging}, {cfg.lookahead}, {cfg.schedule}>")
+            f"{cfg.stages}, {b(cfg.swizzle)}, {cfg.staging}, {cfg.lookahead}, {cfg.schedule}, "
+            f"{b(pers)}>")
 
 
 def measured_traffic(workload: str, cfg, w):
@@ -271,7 +275,7 @@ def measured_traffic(workload: str, cfg, w):
 
 
 def parse_tile(spec):
-    """'256x256x64:2[:swizzle[:group_m[:staging[:WMxWN[:lookahead[:schedule]]]]]]' -> the matching
+    """'256x256x64:2[:swizzle[:group_m[:staging[:WMxWN[:lookahead[:schedule[:persistent]]]]]]]' -> the matching
     compiled configuration (the first one in the table when the wave tile is not given)."""
     import software_pipelined_tiled_gemm_amd as spg
 
@@ -286,11 +290,12 @@ def parse_tile(spec):
     wave = tuple(int(x) for x in parts[5].lower().split("x")) if len(parts) > 5 else None
     look = int(parts[6]) if len(parts) > 6 else 1
     sched = int(parts[7]) if len(parts) > 7 else 0
+    pers = int(parts[8]) if len(parts) > 8 else 0
     for i in range(spg.gemm_num_configs()):
         c = spg.gemm_list_config(i)
         if wave is not None and (c.wave_m, c.wave_n) != wave:
             continue
-        if c.lookahead != look or c.schedule != sched:
+        if c.lookahead != look or c.schedule != sched or c.persistent != pers:
             continue
         if (c.block_m, c.block_n, c.block_k, c.stages, c.swizzle, c.staging) == (bm, bn, bk, st, swz, stg):
             if gm:
@@ -315,6 +320,7 @@ ABLATIONS = [
     ("256x128 tile, 8 waves of 64x64, S=3", "256x128x64:3:1:8:0:64x64:1:0"),
     ("256x128 tile, wave-specialized (producer wave + 4 consumers)", "256x128x64:3:1:8:3:128x64:1:0"),
     ("128x128 tile, 4 waves of 64x64, S=3", "128x128x64:3:1:8:0:64x64:1:0"),
+    ("persistent: one workgroup per CU, its tiles as one k-tile stream", "256x256x64:2:1:8:0:128x64:1:0:1"),
 ]
 
 
@@ -341,7 +347,7 @@ def main():
     ap.add_argument("--workload", default="nn_bf16_8192",
                     help="workload name from workloads.WORKLOADS")
     ap.add_argument("--tile", default=None,
-                    help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging[:WMxWN[:lookahead[:schedule]]]]]] "
+                    help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging[:WMxWN[:lookahead[:schedule[:persistent]]]]]]] "
                          "(default: the library's choice)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra lines (fp16 8192^3, the 8-GPU shard, the standalone "

@@ -88,6 +88,16 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1, GEMM_EPI_RELU = 2 } ge
  *                       followed by its copy op and LDS reads, the TileLang
  *                       tutorial's manual stage/order placement); 1 = the same
  *                       instructions placed by the compiler (its planned pipeline)
+ *   persistent          1 = one workgroup per compute unit, each computing the tiles
+ *                       g, g + G, g + 2G, ... (G = workgroups) as one continuous
+ *                       pipeline of k-tiles, so the copies of a tile's first k-tiles
+ *                       overlap the previous tile's last ones and its epilogue (an
+ *                       extension of this library: the pages pipeline the K loop of
+ *                       one output block); the epilogue stages through a further
+ *                       32 x wave_n x 2 bytes of LDS per wave.  Used only when
+ *                       K % block_k == 0, the output is fp16/bf16 and, for GEMM_B_KN,
+ *                       N % block_n == 0; other problems run the same tile with one
+ *                       workgroup per tile.  0 = one workgroup per tile.
  * The LDS a configuration needs is stages * (block_m + block_n) * block_k * 2 bytes
  * (the shared-memory bound of the TileLang tutorial's shared_bytes()), at most 160 KiB. */
 typedef struct {
@@ -100,6 +110,7 @@ typedef struct {
     int32_t staging;
     int32_t lookahead;
     int32_t schedule;
+    int32_t persistent;
 } gemm_tile_config;
 
 typedef struct gemm_plan* gemm_handle;

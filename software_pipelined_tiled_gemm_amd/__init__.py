@@ -40,7 +40,8 @@ class TileConfig(ctypes.Structure):
                 ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32),
                 ("swizzle", ctypes.c_int32), ("group_m", ctypes.c_int32),
                 ("xcd_remap", ctypes.c_int32), ("staging", ctypes.c_int32),
-                ("lookahead", ctypes.c_int32), ("schedule", ctypes.c_int32)]
+                ("lookahead", ctypes.c_int32), ("schedule", ctypes.c_int32),
+                ("persistent", ctypes.c_int32)]
 
     def __init__(self, **kw):
         kw.setdefault("lookahead", 1)
@@ -62,7 +63,8 @@ class TileConfig(ctypes.Structure):
                 f"wave {d['wave_m']}x{d['wave_n']}, swizzle={d['swizzle']}, "
                 f"group_m={d['group_m']}, xcd_remap={d['xcd_remap']}, "
                 f"staging={STAGING.get(d['staging'], d['staging'])}, lookahead={d['lookahead']}, "
-                f"schedule={'compiler' if d['schedule'] else 'manual'})")
+                f"schedule={'compiler' if d['schedule'] else 'manual'}"
+                f"{', persistent' if d['persistent'] else ''})")
 
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_get_config", "gemm_autotune",

@@ -54,17 +54,20 @@ struct Variant {
     launch_fn fn[2][2];  // [bf16][b_nk]
 };
 
-#define SPG_V(unit, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED)                                    \
-    Variant{{BM, BN, BK, S, WM, WN, SWZ, 0, 1, LDM, PF, SCHED},                                    \
-            {{launch_pipelined<false, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF, SCHED>,   \
-              launch_pipelined<false, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF, SCHED>},   \
-             {launch_pipelined<true, false, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF, SCHED>,    \
-              launch_pipelined<true, true, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF, SCHED>}}},
+#define SPG_LP(BF, NK, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED, PERS) \
+    launch_pipelined<BF, NK, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF, SCHED, (PERS != 0)>
+#define SPG_V(unit, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED, PERS)                              \
+    Variant{{BM, BN, BK, S, WM, WN, SWZ, 0, 1, LDM, PF, SCHED, PERS},                              \
+            {{SPG_LP(false, false, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED, PERS),             \
+              SPG_LP(false, true, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED, PERS)},             \
+             {SPG_LP(true, false, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED, PERS),              \
+              SPG_LP(true, true, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED, PERS)}}},
 
 const Variant kVariants[] = {
 #include "variants.inc"
 };
 #undef SPG_V
+#undef SPG_LP
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 constexpr int kDefaultGroupM = 4;
 
@@ -83,7 +86,7 @@ bool same_tile(const gemm_tile_config& a, const gemm_tile_config& b) {
     return a.block_m == b.block_m && a.block_n == b.block_n && a.block_k == b.block_k &&
            a.stages == b.stages && a.wave_m == b.wave_m && a.wave_n == b.wave_n &&
            a.swizzle == b.swizzle && a.staging == b.staging && a.lookahead == b.lookahead &&
-           a.schedule == b.schedule;
+           a.schedule == b.schedule && a.persistent == b.persistent;
 }
 
 const Variant* find_variant(const gemm_tile_config& c) {
@@ -128,14 +131,27 @@ bool pipelined_fits(int64_t M, int64_t N, int64_t K, gemm_b_layout bl) {
 }
 
 const Variant* find_cfg(int bm, int bn, int bk, int stages, int staging, int wm, int wn,
-                        int lookahead = 1) {
+                        int persistent = 0) {
     for (const Variant& v : kVariants)
         if (v.cfg.block_m == bm && v.cfg.block_n == bn && v.cfg.block_k == bk &&
             v.cfg.stages == stages && v.cfg.staging == staging && v.cfg.swizzle == 1 &&
-            v.cfg.wave_m == wm && v.cfg.wave_n == wn && v.cfg.lookahead == lookahead &&
-            v.cfg.schedule == 0)
+            v.cfg.wave_m == wm && v.cfg.wave_n == wn && v.cfg.lookahead == 1 &&
+            v.cfg.schedule == 0 && v.cfg.persistent == persistent)
             return &v;
     return nullptr;
+}
+
+// Compute units of the current device (cached per device; 0 if the query fails).
+int cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 0;
+    __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+    return n;
 }
 
 gemm_tile_config heuristic(int64_t M, int64_t N) {
@@ -178,7 +194,18 @@ KArgs make_args(const gemm_plan* p, const void* A, const void* B, void* C, int b
     a.xcd_remap = p->cfg.xcd_remap ? 1 : 0;
     a.out_dtype = (int32_t)p->out;
     a.epilogue = (int32_t)p->epi;
+    a.persistent = 0;
     return a;
+}
+
+// Shapes the persistent kernel takes: every k-tile whole (K % block_k == 0), a
+// 16-bit output (its epilogue staging holds 2-byte values) and, for B stored
+// [K,N], whole column tiles (its copies carry no column masks).
+bool persistent_fits(const gemm_plan* p, const gemm_tile_config& c) {
+    if (!c.persistent || c.block_k <= 0 || c.block_n <= 0) return false;
+    if (p->out == GEMM_F32 || p->K % c.block_k != 0) return false;
+    if (p->bl == GEMM_B_KN && p->N % c.block_n != 0) return false;
+    return true;
 }
 
 gemm_status launch_plan(const gemm_plan* p, const gemm_tile_config& cfg, const Variant* var,
@@ -197,7 +224,16 @@ gemm_status launch_plan(const gemm_plan* p, const gemm_tile_config& cfg, const V
         gemm_plan q = *p;
         q.cfg = cfg;
         KArgs a = make_args(&q, A, B, C, cfg.block_m, cfg.block_n);
-        dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
+        int64_t wgs = (int64_t)a.tiles_m * a.tiles_n;
+        if (persistent_fits(p, cfg)) {
+            // one workgroup per CU (its LDS allows no second), each walking its tiles
+            const int cus = cu_count();
+            if (cus > 0) {
+                a.persistent = 1;
+                wgs = std::min<int64_t>(wgs, cus);
+            }
+        }
+        dim3 grid((unsigned)wgs);
         var->fn[bf ? 1 : 0][nk ? 1 : 0](a, grid, st);
     }
     hipError_t e = hipGetLastError();
@@ -257,7 +293,8 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
             (force->xcd_remap != 0 && force->xcd_remap != 1) ||
             force->staging < 0 || force->staging > 3 ||
             (force->lookahead != 1 && force->lookahead != 2) ||
-            (force->schedule != 0 && force->schedule != 1))
+            (force->schedule != 0 && force->schedule != 1) ||
+            (force->persistent != 0 && force->persistent != 1))
             return GEMM_ERR_INVALID_ARG;
         if (gemm_lds_bytes(force) > 160 * 1024) return GEMM_ERR_UNSUPPORTED;
         var = find_variant(*force);

@@ -85,6 +85,7 @@ struct KArgs {
     int32_t xcd_remap;
     int32_t out_dtype;
     int32_t epilogue;
+    int32_t persistent;   // launcher only: run the persistent instantiation (grid = CUs)
 };
 
 // ---------------------------------------------------------------------------
@@ -350,13 +351,25 @@ __device__ __forceinline__ int kswz_t(int r) {
 // step followed by its copy op and LDS reads and a scheduling barrier (the
 // TileLang tutorial's manual stage/order placement); 1 = the compiler, with the
 // same instructions and no scheduling barriers (its compiler-planned pipeline).
+//
+// PERS (persistent): the grid holds one workgroup per CU and workgroup w computes
+// tiles w, w + G, w + 2G, ... (G = grid size) as one continuous stream of k-tiles,
+// so the copies issued during the last k-tiles of a tile already fetch the first
+// k-tiles of the next one, and the fragment lookahead runs across the tile
+// boundary.  Each tile's epilogue goes through a staging area of its own (the ring
+// stays busy with the next tile's copies) and no workgroup-wide barrier is added.
+// The launcher uses it only when K % BK == 0 (no partial k-tile), the output is
+// 16-bit and, for B stored [K,N], N % BN == 0 (no column masks on the copies).
 template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ, int LDM,
-          int PF, int SCHED>
+          int PF, int SCHED, bool PERS>
 __global__ void __launch_bounds__((Geom<BM, BN, BK, WM, WN, S>::NT))
 pipelined_gemm(KArgs args) {
     using G = Geom<BM, BN, BK, WM, WN, S>;
     static_assert(LDM != 2 || S >= 3, "spread copies need a slot of slack");
     static_assert(PF == 1 || (PF == 2 && BK == 64 && S > 1), "lookahead 2 needs four k-steps per k-tile");
+    static_assert(!PERS || (LDM == 0 && S >= 2), "persistent: direct copies and a ring of >= 2 slots");
+    static_assert(!PERS || S * G::STAGE + G::NW * 32 * WN * 2 <= 160 * 1024,
+                  "persistent: ring + epilogue staging must fit the LDS");
     constexpr int TM = G::TM, TN = G::TN, A_BYTES = G::A_BYTES, KSTEPS = G::KSTEPS;
     constexpr int ROWB = G::ROWB;
     constexpr int A_DMA = G::A_DMA, B_DMA = G::B_DMA;
@@ -527,6 +540,49 @@ pipelined_gemm(KArgs args) {
         static_for<0, G::L>([&](auto jc) { dma_op(slot, src, jc, first); });
     };
 
+    // ---- persistent: the copy side of the k-tile stream ------------------------
+    // (cp_tile, cp_kt) is the next k-tile to copy; cp_* hold the resource bases of
+    // cp_tile (empty once it is past the last tile: those copies read zero).
+    const int T = args.tiles_m * args.tiles_n;
+    int cp_tile = blockIdx.x, cp_kt = 0;
+    bool cp_valid = false;
+    uint64_t cp_a = 0, cp_b = 0;
+    uint32_t cp_an = 0, cp_bn = 0;
+    auto set_copy_tile = [&]() __attribute__((always_inline)) {
+        cp_valid = cp_tile < T;
+        if (cp_valid) {
+            int ctm, ctn;
+            tile_of(cp_tile, args, ctm, ctn);
+            const int cm0 = ctm * BM, cn0 = ctn * BN;
+            const int ar = (M - cm0) < BM ? (M - cm0) : BM;
+            cp_a = (uint64_t)(uintptr_t)(args.A + (size_t)cm0 * K);
+            cp_an = (uint32_t)ar * (uint32_t)K * 2u;
+            if constexpr (B_NK) {
+                const int br = (N - cn0) < BN ? (N - cn0) : BN;
+                cp_b = (uint64_t)(uintptr_t)(args.B + (size_t)cn0 * K);
+                cp_bn = (uint32_t)br * (uint32_t)K * 2u;
+            } else {
+                cp_b = (uint64_t)(uintptr_t)(args.B + cn0);
+                cp_bn = (uint32_t)(((size_t)K * N - cn0) * 2u);
+            }
+        }
+    };
+    // resources of the next k-tile of the stream, then advance (K % BK == 0: every
+    // k-tile of a valid tile lies inside [0, K), so the window never underflows)
+    auto next_copy = [&]() __attribute__((always_inline)) -> DmaSrc {
+        const uint32_t sa = (uint32_t)cp_kt * (uint32_t)(BK * 2);
+        const uint32_t sb = (uint32_t)cp_kt * (uint32_t)BK * b_kb;
+        const DmaSrc r{make_rsrc((const void*)(uintptr_t)(cp_a + sa), cp_valid ? cp_an - sa : 0u),
+                       make_rsrc((const void*)(uintptr_t)(cp_b + sb), cp_valid ? cp_bn - sb : 0u)};
+        if (++cp_kt == nk) {
+            cp_kt = 0;
+            cp_tile += gridDim.x;
+            set_copy_tile();
+        }
+        return r;
+    };
+    if constexpr (PERS) set_copy_tile();
+
     // ---- per-lane LDS read offsets -------------------------------------------
     // A (second MFMA operand): lane l reads row wm*WM + bm*32 + l%32,
     // k = kk*16 + (l/32)*8 .. +7  (16-B chunk 2kk + l/32).  The swizzle depends on
@@ -568,6 +624,27 @@ pipelined_gemm(KArgs args) {
         for (int j = 0; j < TM; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // ---- persistent: the compute side of the k-tile stream ----------------------
+    // (c_tile, c_kt): the tile and k-tile the MFMAs are on.  A tile's epilogue stages
+    // through pstg, 32 rows x WN outputs per wave, apart from the ring.
+    int c_tile = blockIdx.x, c_kt = 0;
+    __shared__ __attribute__((aligned(1024))) char pstg[PERS ? G::NW * 32 * WN * 2 : 16];
+    auto pers_epilogue = [&](auto tile) __attribute__((always_inline)) {
+        int etm, etn;
+        tile_of(tile, args, etm, etn);
+        char* stg = pstg + wave * (32 * WN * 2);
+        const int mb = etm * BM + wm * WM, nb = etn * BN + wn * WN;
+        const int ep = args.epilogue;
+        auto store_as = [&](auto odc) __attribute__((always_inline)) {
+            constexpr int OD = decltype(odc)::value;
+            if (ep == kEpiGelu) store_tile<OD, kEpiGelu, TM, TN, WN>(acc, stg, args, mb, nb, lane);
+            else if (ep == kEpiRelu) store_tile<OD, kEpiRelu, TM, TN, WN>(acc, stg, args, mb, nb, lane);
+            else store_tile<OD, kEpiNone, TM, TN, WN>(acc, stg, args, mb, nb, lane);
+        };
+        if (args.out_dtype == kOutBF16) store_as(std::integral_constant<int, kOutBF16>{});
+        else store_as(std::integral_constant<int, kOutF16>{});
+    };
 
     // Operand fragments of one 16-wide k step: A rows (second MFMA operand) and
     // B columns (first MFMA operand).  Two sets alternate so that the LDS reads of
@@ -734,7 +811,14 @@ pipelined_gemm(KArgs args) {
         const int nt = ((nk + S - 1) / S) * S;
         auto first_of = [](auto sc) { return std::integral_constant<bool, decltype(sc)::value == 0>{}; };
         constexpr int PRE = LDM == 0 ? 0 : PF * CPS;  // ops of k-tile S-1 the window before k-tile 0 moves
-        if constexpr (LDM == 0) {
+        if constexpr (PERS) {
+            // prologue: the first S k-tiles of the stream fill every slot
+            static_for<0, S>([&](auto sc) {
+                const DmaSrc src = next_copy();
+                static_for<0, G::L>([&](auto jc) { dma_op(slot_of(sc), src, jc, NotFirst{}); });
+            });
+            wait_vmcnt<(S - 1) * G::L>();
+        } else if constexpr (LDM == 0) {
             // prologue: k-tiles 0 .. S-1 fill every slot; wait for k-tile 0
             static_for<0, S>([&](auto sc) { issue(slot_of(sc), sc.value, first_of(sc)); });
             wait_vmcnt<(S - 1) * G::L>();
@@ -775,13 +859,18 @@ pipelined_gemm(KArgs args) {
                 if constexpr (LDM == 1) return reg_src(kt);
                 else return dma_src(kt);
             };
-            {
+            if constexpr (LDM == 0) {
+                // all copies of a window are issued right after its barrier
+                static_for<0, KSTEPS - PF>([&](auto kc) {
+                    kstage(kc, cur, nxt, prev, kNoCopy, std::integral_constant<int, -1>{}, T_{});
+                });
+            } else {
                 // the window that started at barrier t-1: k-tile t+S-1 into prev
                 // (register staging: write k-tile t+S-1, load k-tile t+S)
                 const auto src = src_of(LDM == 1 ? t + S : t + S - 1);
                 static_for<0, KSTEPS - PF>([&](auto kc) {
                     constexpr int kk = decltype(kc)::value;
-                    using Pos = std::integral_constant<int, LDM == 0 ? -1 : PF + kk>;
+                    using Pos = std::integral_constant<int, PF + kk>;
                     kstage(kc, cur, nxt, prev, src, Pos{}, T_{});
                 });
             }
@@ -797,7 +886,10 @@ pipelined_gemm(KArgs args) {
             {
                 // the window that starts here: k-tile t+S into cur
                 // (register staging: write k-tile t+S, load k-tile t+S+1)
-                const auto src = src_of(LDM == 1 ? t + S + 1 : t + S);
+                const auto src = [&]() __attribute__((always_inline)) {
+                    if constexpr (PERS) return next_copy();
+                    else return src_of(LDM == 1 ? t + S + 1 : t + S);
+                }();
                 static_for<KSTEPS - PF, KSTEPS>([&](auto kc) {
                     constexpr int kk = decltype(kc)::value;
                     using Pos = std::integral_constant<int, kk - (KSTEPS - PF)>;
@@ -805,37 +897,67 @@ pipelined_gemm(KArgs args) {
                 });
             }
             __builtin_amdgcn_s_setprio(0);
+            if constexpr (PERS) {
+                // the MFMAs of the tile's last k-tile are issued: store it, start the next
+                if (++c_kt == nk) {
+                    if (c_tile < T) pers_epilogue(c_tile);
+                    c_kt = 0;
+                    c_tile += gridDim.x;
+#pragma unroll
+                    for (int i = 0; i < TN; ++i)
+#pragma unroll
+                        for (int j = 0; j < TM; ++j)
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+                }
+            }
         };
-        for (int t0 = 0; t0 < nt; t0 += S) {
-            static_for<0, S>([&](auto sc) { ktile(sc, t0 + decltype(sc)::value); });
+        if constexpr (PERS) {
+            // this workgroup's tiles as one stream of k-tiles, in whole S-groups (the
+            // k-tiles past its last tile are zeros and nothing is stored for them)
+            const int mine = (T - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+            const int ns = ((mine * nk + S - 1) / S) * S;
+            for (int t0 = 0; t0 < ns; t0 += S) {
+                static_for<0, S>([&](auto sc) { ktile(sc, t0 + decltype(sc)::value); });
+            }
+        } else {
+            for (int t0 = 0; t0 < nt; t0 += S) {
+                static_for<0, S>([&](auto sc) { ktile(sc, t0 + decltype(sc)::value); });
+            }
         }
     }
 
     // ---- epilogue ------------------------------------------------------------
-    // the loop leaves zero-fill copies of k-tiles >= nt in flight: let them land
-    // before the ring is reused for staging
-    wait_vmcnt<0>();
-    __syncthreads();  // the ring is drained and free for staging
-    char* stg;
-    {
-        const int sl = wave % S;
-        char* base = sl == 0 ? ring0 : sl == 1 ? ring1 : sl == 2 ? ring2 : sl == 3 ? ring3
-                   : sl == 4 ? ring4 : ring5;
-        stg = base + (wave / S) * G::STG;
+    if constexpr (PERS) {
+        // every tile is stored; the zero-fill copies past the stream must land
+        // before the workgroup ends
+        wait_vmcnt<0>();
+    } else {
+        // the loop leaves zero-fill copies of k-tiles >= nt in flight: let them land
+        // before the ring is reused for staging
+        wait_vmcnt<0>();
+        __syncthreads();  // the ring is drained and free for staging
+        char* stg;
+        {
+            const int sl = wave % S;
+            char* base = sl == 0 ? ring0 : sl == 1 ? ring1 : sl == 2 ? ring2 : sl == 3 ? ring3
+                       : sl == 4 ? ring4 : ring5;
+            stg = base + (wave / S) * G::STG;
+        }
+        // one branch on the (uniform) output type and epilogue, outside all accumulator reads
+        const int od = args.out_dtype;
+        const int ep = args.epilogue;
+        const int m_base = m0 + wm * WM, n_base = n0 + wn * WN;
+        auto store_as = [&](auto odc) __attribute__((always_inline)) {
+            constexpr int OD = decltype(odc)::value;
+            if (ep == kEpiGelu) store_tile<OD, kEpiGelu, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+            else if (ep == kEpiRelu) store_tile<OD, kEpiRelu, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+            else store_tile<OD, kEpiNone, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+        };
+        if (od == kOutF32) store_as(std::integral_constant<int, kOutF32>{});
+        else if (od == kOutBF16) store_as(std::integral_constant<int, kOutBF16>{});
+        else store_as(std::integral_constant<int, kOutF16>{});
     }
-    // one branch on the (uniform) output type and epilogue, outside all accumulator reads
-    const int od = args.out_dtype;
-    const int ep = args.epilogue;
-    const int m_base = m0 + wm * WM, n_base = n0 + wn * WN;
-    auto store_as = [&](auto odc) __attribute__((always_inline)) {
-        constexpr int OD = decltype(odc)::value;
-        if (ep == kEpiGelu) store_tile<OD, kEpiGelu, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
-        else if (ep == kEpiRelu) store_tile<OD, kEpiRelu, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
-        else store_tile<OD, kEpiNone, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
-    };
-    if (od == kOutF32) store_as(std::integral_constant<int, kOutF32>{});
-    else if (od == kOutBF16) store_as(std::integral_constant<int, kOutBF16>{});
-    else store_as(std::integral_constant<int, kOutF16>{});
 }
 
 // ---------------------------------------------------------------------------

@@ -3,7 +3,7 @@
 #define SPG_DEFINE_LAUNCHERS
 #include "launch.hpp"
 
-#define SPG_V(unit, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED) SPG_V_##unit(BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED)
+#define SPG_V(unit, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED, PERS) SPG_V_##unit(BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED, PERS)
 #define SPG_V_0(...)
 #define SPG_V_1(...)
 #define SPG_V_2(...)
@@ -27,4 +27,5 @@
 #define SPG_V_20(...) SPG_INSTANTIATE_ALL(__VA_ARGS__)
 #define SPG_V_21(...)
 #define SPG_V_22(...)
+#define SPG_V_23(...)
 #include "variants.inc"

@@ -120,6 +120,12 @@ def test_forced_configs(L):
     with pytest.raises(spg.GemmError) as e:
         spg.gemm_create(512, 512, 512, force=sch)
     assert e.value.status == 1
+    per = spg.TileConfig(block_m=256, block_n=256, block_k=64, stages=2, wave_m=128,
+                         wave_n=64, swizzle=1, group_m=4, xcd_remap=1, persistent=2)
+    with pytest.raises(spg.GemmError) as e:
+        spg.gemm_create(512, 512, 512, force=per)
+    assert e.value.status == 1
+    assert any(spg.gemm_list_config(i).persistent for i in range(n))
     for look in (0, 3):
         far = spg.TileConfig(block_m=256, block_n=256, block_k=64, stages=2, wave_m=128,
                              wave_n=128, swizzle=1, group_m=4, xcd_remap=1, lookahead=look)

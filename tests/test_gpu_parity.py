@@ -179,6 +179,63 @@ def test_largest_pipelined_operands(case):
     _log(f"  err_q={res['err_q']:.3e}")
 
 
+def _persistent_pair():
+    """The persistent configuration and the same tile with one workgroup per tile."""
+    pers = [c for c in _variants() if c.persistent]
+    assert pers, "no persistent configuration compiled"
+    p = pers[0]
+    for c in _variants():
+        d, e = c.as_dict(), p.as_dict()
+        d.pop("persistent"), e.pop("persistent")
+        if d == e and not c.persistent:
+            return p, c
+    raise AssertionError("the persistent tile has no one-tile-per-workgroup twin")
+
+
+# (M, N, K, layout): more tiles than CUs (some workgroups take two or three tiles),
+# ragged M (and N for [N,K]), k-tile counts that are odd, one, and not a multiple of
+# the ring depth, and a grid smaller than the CU count
+PERSISTENT_SHAPES = [(4100, 4352, 192, W.B_KN), (4100, 4200, 128, W.B_NK),
+                     (2056, 8192, 64, W.B_KN), (520, 768, 320, W.B_NK), (300, 256, 64, W.B_KN),
+                     (8200, 8192, 64, W.B_NK)]
+
+
+@pytest.mark.parametrize("shape", PERSISTENT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_persistent_matches_oracle_and_twin(shape):
+    M, N, K, layout = shape
+    pers, twin = _persistent_pair()
+    for in_dtype, out_dtype, epi in ((W.BF16, W.BF16, "none"), (W.F16, W.F16, "gelu_tanh"),
+                                     (W.BF16, W.F16, "relu")):
+        w = W.custom(M, N, K, in_dtype, out_dtype, layout, epi, ("uniform", -1.0, 1.0))
+        a, b = W.make_inputs(w)
+        _log(f"persistent {pers} {w.describe()}")
+        C, used = G.run(w, a, b, force=pers)
+        assert used.persistent == 1
+        got = G.c_values(C, w)
+        big = M * N > 4_000_000
+        rows = np.unique(np.r_[0, 255, 256, M - 1, np.arange(0, M, 97)]) if big else None
+        G.check(w, a, b, got[rows] if big else got, rows=rows)
+        # the same tile, one workgroup per tile: the same k order, so the same bits
+        C2, _ = G.run(w, a, b, force=twin)
+        assert np.array_equal(G.c_values(C2, w), got)
+
+
+def test_persistent_falls_back_where_it_does_not_apply():
+    # fp32 output, K % 64 != 0, [K,N] with N % 256 != 0: the persistent tile runs one
+    # workgroup per tile, with the same result as its twin
+    pers, twin = _persistent_pair()
+    for (M, N, K, layout, out) in ((600, 512, 256, W.B_KN, W.F32), (600, 512, 200, W.B_NK, W.BF16),
+                                   (600, 520, 256, W.B_KN, W.F16)):
+        w = W.custom(M, N, K, W.BF16, out, layout, "gelu_tanh", ("uniform", -1.0, 1.0))
+        a, b = W.make_inputs(w)
+        _log(f"persistent fallback {w.describe()}")
+        C, _ = G.run(w, a, b, force=pers)
+        got = G.c_values(C, w)
+        G.check(w, a, b, got)
+        C2, _ = G.run(w, a, b, force=twin)
+        assert np.array_equal(G.c_values(C2, w), got)
+
+
 def test_autotune_keeps_parity():
     w = W.custom(1024, 768, 512, W.F16, W.F16, W.B_NK)
     a, b = W.make_inputs(w)
