@@ -217,73 +217,99 @@ __device__ __forceinline__ floatx16 mfma(const u32x4& x, const u32x4& y, const f
 // ---------------------------------------------------------------------------
 
 // Epilogue of one wave: accumulator -> (GELU / ReLU) -> output type -> LDS staging ->
-// 16-byte row-contiguous global stores.  The wave's C tile is processed 32 rows
-// (one MFMA block row) at a time through a private 32 x WN staging buffer whose
-// 16-B chunks are XOR-swizzled by row so that both the 4-value writes (32 rows,
-// same column) and the row reads are free of bank conflicts.
-template <int OD, int EPI, int TM, int TN, int WN>
+// 16-byte row-contiguous global stores.  The wave's C tile is processed in 32-row
+// blocks (one MFMA block row), NP blocks per round: a round writes its blocks into NP
+// private 32 x WN staging buffers, then reads them back row by row and stores them, so
+// the LDS write -> read -> store latency is paid once per round rather than per block.
+// The 16-B chunks of a staged row are XOR-swizzled by row so that both the 4-value
+// writes (32 rows, same column) and the row reads are free of bank conflicts.
+template <int OD, int EPI, int TM, int TN, int WN, int NP = 1>
 __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TN][TM], char* stg,
                                            const KArgs& args, int m_base, int n_base, int lane) {
     constexpr int OB = OD == kOutF32 ? 4 : 2;         // output bytes
     constexpr int ROWB = WN * OB;                     // staged row bytes
     constexpr int CPR = ROWB / 16;                    // 16-B chunks per staged row
     constexpr int E16 = 16 / OB;                      // outputs per chunk
+    constexpr int PASSB = 32 * ROWB;                  // staging bytes of one block
     static_assert(CPR == 8 || CPR == 16 || CPR == 32, "staging swizzle assumes 8..32 chunks");
+    static_assert(NP >= 1 && TM % NP == 0, "blocks per round must divide the wave's blocks");
     auto swz = [](int row) { return CPR >= 16 ? (row & 15) : ((row >> 1) & 7); };
     const int M = args.M, N = args.N;
     const bool vec_ok = (N % E16) == 0;
     const int lrow = lane & 31;
 #pragma unroll
-    for (int bm = 0; bm < TM; ++bm) {
-        // 1) lane holds C[row l%32][cols bn*32 + 8q + 4(l/32) + 0..3]
+    for (int g = 0; g < TM; g += NP) {
+        // one round at a time: keeps the accumulator reads of later rounds from being
+        // hoisted into this one (with 256 accumulators that spills registers)
+        __builtin_amdgcn_sched_barrier(0);
+        // 1) lane holds C[row l%32][cols bn*32 + 8q + 4(l/32) + 0..3] of block g+p
 #pragma unroll
-        for (int bn = 0; bn < TN; ++bn) {
+        for (int p = 0; p < NP; ++p) {
+            const int bm = g + p;
+            char* sp = stg + p * PASSB;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float v[4];
+            for (int bn = 0; bn < TN; ++bn) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[e] = acc[bn][bm][4 * q + e];
-                    v[e] = epi_t<EPI>(v[e]);
-                }
-                const int byte = (bn * 32 + 8 * q + 4 * (lane >> 5)) * OB;
-                char* dst = stg + lrow * ROWB + (((byte >> 4) ^ swz(lrow)) << 4) + (byte & 15);
-                if constexpr (OD == kOutF32) {
-                    *(SPG_LDS u32x4*)dst = u32x4{__builtin_bit_cast(uint32_t, v[0]),
-                                                 __builtin_bit_cast(uint32_t, v[1]),
-                                                 __builtin_bit_cast(uint32_t, v[2]),
-                                                 __builtin_bit_cast(uint32_t, v[3])};
-                } else {
-                    constexpr bool BF = OD == kOutBF16;
-                    const uint32_t p0 = (uint32_t)f32_to_bits(v[0], BF) | ((uint32_t)f32_to_bits(v[1], BF) << 16);
-                    const uint32_t p1 = (uint32_t)f32_to_bits(v[2], BF) | ((uint32_t)f32_to_bits(v[3], BF) << 16);
-                    *(SPG_LDS u32x2*)dst = u32x2{p0, p1};
+                for (int q = 0; q < 4; ++q) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[e] = acc[bn][bm][4 * q + e];
+                        v[e] = epi_t<EPI>(v[e]);
+                    }
+                    const int byte = (bn * 32 + 8 * q + 4 * (lane >> 5)) * OB;
+                    char* dst = sp + lrow * ROWB + (((byte >> 4) ^ swz(lrow)) << 4) + (byte & 15);
+                    if constexpr (OD == kOutF32) {
+                        *(SPG_LDS u32x4*)dst = u32x4{__builtin_bit_cast(uint32_t, v[0]),
+                                                     __builtin_bit_cast(uint32_t, v[1]),
+                                                     __builtin_bit_cast(uint32_t, v[2]),
+                                                     __builtin_bit_cast(uint32_t, v[3])};
+                    } else {
+                        constexpr bool BF = OD == kOutBF16;
+                        const uint32_t p0 = (uint32_t)f32_to_bits(v[0], BF) | ((uint32_t)f32_to_bits(v[1], BF) << 16);
+                        const uint32_t p1 = (uint32_t)f32_to_bits(v[2], BF) | ((uint32_t)f32_to_bits(v[3], BF) << 16);
+                        *(SPG_LDS u32x2*)dst = u32x2{p0, p1};
+                    }
                 }
             }
         }
         // 2) LDS -> global, 16 B per lane, consecutive lanes along a row
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int bm = g + p;
+            const char* sp = stg + p * PASSB;
 #pragma unroll 1
-        for (int it = 0; it < (32 * CPR) / 64; ++it) {
-            const int idx = it * 64 + lane;
-            const int row = idx / CPR;
-            const int ch = idx % CPR;
-            const u32x4 val = *(const SPG_LDS u32x4*)(stg + row * ROWB + ((ch ^ swz(row)) << 4));
-            const int gm = m_base + bm * 32 + row;
-            const int gn = n_base + ch * E16;
-            if (gm < M && gn < N) {
-                char* dstg = (char*)args.C + ((size_t)gm * N + gn) * OB;
-                if (vec_ok && gn + E16 <= N) {
-                    *(u32x4*)dstg = val;
-                } else {
-                    const int lim = (N - gn) < E16 ? (N - gn) : E16;
-                    for (int e = 0; e < lim; ++e) {
-                        if constexpr (OB == 4) ((uint32_t*)dstg)[e] = val[e];
-                        else ((uint16_t*)dstg)[e] = (uint16_t)(val[e >> 1] >> ((e & 1) * 16));
+            for (int it = 0; it < (32 * CPR) / 64; ++it) {
+                const int idx = it * 64 + lane;
+                const int row = idx / CPR;
+                const int ch = idx % CPR;
+                const u32x4 val = *(const SPG_LDS u32x4*)(sp + row * ROWB + ((ch ^ swz(row)) << 4));
+                const int gm = m_base + bm * 32 + row;
+                const int gn = n_base + ch * E16;
+                if (gm < M && gn < N) {
+                    char* dstg = (char*)args.C + ((size_t)gm * N + gn) * OB;
+                    if (vec_ok && gn + E16 <= N) {
+                        *(u32x4*)dstg = val;
+                    } else {
+                        const int lim = (N - gn) < E16 ? (N - gn) : E16;
+                        for (int e = 0; e < lim; ++e) {
+                            if constexpr (OB == 4) ((uint32_t*)dstg)[e] = val[e];
+                            else ((uint16_t*)dstg)[e] = (uint16_t)(val[e >> 1] >> ((e & 1) * 16));
+                        }
                     }
                 }
             }
         }
     }
+}
+
+// Largest number of 32-row blocks (a divisor of TM) whose staging fits `budget` bytes.
+template <int TM, int WN, int OB>
+constexpr int blocks_per_round(int budget) {
+    int np = 1;
+    for (int d = 1; d <= TM; ++d)
+        if (TM % d == 0 && d * 32 * WN * OB <= budget) np = d;
+    return np;
 }
 
 // Workgroup barrier for LDS hazards only: this wave's LDS operations have
@@ -312,7 +338,9 @@ struct Geom {
     static constexpr int A_DMA = A_BYTES / 1024 / NW;  // DMA instructions per wave per k-tile
     static constexpr int B_DMA = B_BYTES / 1024 / NW;
     static constexpr int L = A_DMA + B_DMA;
-    static constexpr int STG = 32 * WN * 4;            // epilogue staging bytes per wave (fp32 worst case)
+    static constexpr int STG = 32 * WN * 4;            // epilogue staging bytes of one fp32 block
+    // epilogue staging available per wave: a ring slot shared by ceil(NW / S) waves
+    static constexpr int STGW = (STAGE / ((NW + S - 1) / S)) / 16 * 16;
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile shape");
     static_assert(BN >= 128, "[K,N] swizzle needs 16 chunks per row");
@@ -942,7 +970,7 @@ pipelined_gemm(KArgs args) {
             const int sl = wave % S;
             char* base = sl == 0 ? ring0 : sl == 1 ? ring1 : sl == 2 ? ring2 : sl == 3 ? ring3
                        : sl == 4 ? ring4 : ring5;
-            stg = base + (wave / S) * G::STG;
+            stg = base + (wave / S) * G::STGW;
         }
         // one branch on the (uniform) output type and epilogue, outside all accumulator reads
         const int od = args.out_dtype;
@@ -950,9 +978,12 @@ pipelined_gemm(KArgs args) {
         const int m_base = m0 + wm * WM, n_base = n0 + wn * WN;
         auto store_as = [&](auto odc) __attribute__((always_inline)) {
             constexpr int OD = decltype(odc)::value;
-            if (ep == kEpiGelu) store_tile<OD, kEpiGelu, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
-            else if (ep == kEpiRelu) store_tile<OD, kEpiRelu, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
-            else store_tile<OD, kEpiNone, TM, TN, WN>(acc, stg, args, m_base, n_base, lane);
+            // several blocks per round only for one wave per SIMD: with two, the partner
+            // wave already covers the latency (measured: +1.2% with 4 waves, -0.4% with 8)
+            constexpr int NP = G::NW > 4 ? 1 : blocks_per_round<TM, WN, OD == kOutF32 ? 4 : 2>(G::STGW);
+            if (ep == kEpiGelu) store_tile<OD, kEpiGelu, TM, TN, WN, NP>(acc, stg, args, m_base, n_base, lane);
+            else if (ep == kEpiRelu) store_tile<OD, kEpiRelu, TM, TN, WN, NP>(acc, stg, args, m_base, n_base, lane);
+            else store_tile<OD, kEpiNone, TM, TN, WN, NP>(acc, stg, args, m_base, n_base, lane);
         };
         if (od == kOutF32) store_as(std::integral_constant<int, kOutF32>{});
         else if (od == kOutBF16) store_as(std::integral_constant<int, kOutBF16>{});
