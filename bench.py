@@ -308,7 +308,8 @@ def parse_tile(spec):
 # distinct kernel instantiation, so a profiler run over `--ablations` attributes
 # counters to the rows by kernel name.
 ABLATIONS = [
-    ("default: 256x256x64, S=2, 8 waves of 128x64, direct copies", "256x256x64:2:1:8:0:128x64:1:0"),
+    ("default: 256x256x64, S=2, 8 waves of 128x64, direct copies, A one slot deeper", "256x256x64:2:1:8:4:128x64:1:0"),
+    ("A and B rings both two deep (staging 0)", "256x256x64:2:1:8:0:128x64:1:0"),
     ("no overlap (S=1, the serial loop), 4 waves", "256x256x64:1:1:8:0:128x128:1:0"),
     ("4 waves of 128x128 (one per SIMD), lookahead 1", "256x256x64:2:1:8:0:128x128:1:0"),
     ("4 waves of 128x128, lookahead 2", "256x256x64:2:1:8:0:128x128:2:0"),

@@ -80,7 +80,10 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1, GEMM_EPI_RELU = 2 } ge
  *                       3 = wave-specialized (the Pallas guide's warp-specialized
  *                       pipeline): one producer wave issues every copy, the
  *                       consumer waves only read LDS and multiply, and per-slot
- *                       counters in LDS replace the barrier
+ *                       counters in LDS replace the barrier;
+ *                       4 = as 0, with A in a ring one slot deeper than B (stages =
+ *                       2: three A slots, two B slots), so the copies of A have two
+ *                       k-tiles to land and those of B one
  *   lookahead           MFMA k-steps between the LDS read of an operand fragment and
  *                       its use: 1 (two fragment sets in registers) or 2 (four sets;
  *                       block_k 64, stages >= 2)
@@ -99,7 +102,8 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1, GEMM_EPI_RELU = 2 } ge
  *                       N % block_n == 0; other problems run the same tile with one
  *                       workgroup per tile.  0 = one workgroup per tile.
  * The LDS a configuration needs is stages * (block_m + block_n) * block_k * 2 bytes
- * (the shared-memory bound of the TileLang tutorial's shared_bytes()), at most 160 KiB. */
+ * (the shared-memory bound of the TileLang tutorial's shared_bytes()), plus
+ * block_m * block_k * 2 for staging 4, at most 160 KiB. */
 typedef struct {
     int32_t block_m, block_n, block_k;
     int32_t stages;
@@ -151,7 +155,8 @@ gemm_status gemm_autotune(gemm_handle h, const void* A, const void* B, void* C,
 int32_t gemm_num_configs(void);
 gemm_status gemm_list_config(int32_t index, gemm_tile_config* out);
 
-/* LDS bytes a configuration needs: stages * (block_m + block_n) * block_k * 2. */
+/* LDS bytes a configuration needs: stages * (block_m + block_n) * block_k * 2, plus
+ * block_m * block_k * 2 for staging 4. */
 int64_t gemm_lds_bytes(const gemm_tile_config* cfg);
 
 /* Human-readable name of a status code (static storage). */

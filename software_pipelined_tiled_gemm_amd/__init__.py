@@ -25,7 +25,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "out of memory",
 DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
 B_LAYOUTS = {"kn": 0, "nk": 1}
 EPILOGUES = {"none": 0, "gelu_tanh": 1, "relu": 2}
-STAGING = {0: "direct", 1: "vgpr", 2: "direct-spread", 3: "producer-wave"}
+STAGING = {0: "direct", 1: "vgpr", 2: "direct-spread", 3: "producer-wave", 4: "direct-a-deep"}
 
 
 class GemmError(RuntimeError):

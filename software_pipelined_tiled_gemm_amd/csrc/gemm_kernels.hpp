@@ -368,6 +368,13 @@ __device__ __forceinline__ int kswz_t(int r) {
 //      to the next (L / KSTEPS per stage), so the vector-memory queue never
 //      backs up into the MFMA issue of a wave that is alone on its SIMD.  The
 //      last copies of a window land one k-tile before they are read, hence S >= 3.
+//   4  direct-to-LDS copies as in 0, with the A operand in a ring one slot deeper
+//      than B (S = 2: three A slots, two B slots).  The window after barrier t copies
+//      B of k-tile t+2 and A of k-tile t+3, so A has two k-tiles to land instead of
+//      one; the B copies are issued first, and the wait before barrier t+1 leaves the
+//      A copies of k-tile t+3 in flight.  With the tile raster's 8 x 4 blocks of
+//      tiles per XCD, A carries 2/3 of the bytes that miss L2.  The loop is unrolled
+//      by 6 k-tiles (three A slots x two B slots), plus an unrolled tail.
 //
 // PF (lookahead) is the number of MFMA k-steps between the LDS read of an operand
 // fragment and its use: 1 keeps two fragment sets in registers, 2 keeps four and
@@ -396,6 +403,8 @@ pipelined_gemm(KArgs args) {
     static_assert(LDM != 2 || S >= 3, "spread copies need a slot of slack");
     static_assert(PF == 1 || (PF == 2 && BK == 64 && S > 1), "lookahead 2 needs four k-steps per k-tile");
     static_assert(!PERS || (LDM == 0 && S >= 2), "persistent: direct copies and a ring of >= 2 slots");
+    static_assert(LDM != 4 || (S == 2 && S * G::STAGE + G::A_BYTES <= 160 * 1024),
+                  "A-deep ring: two slots plus one more A slot within the LDS");
     static_assert(!PERS || S * G::STAGE + G::NW * 32 * WN * 2 <= 160 * 1024,
                   "persistent: ring + epilogue staging must fit the LDS");
     constexpr int TM = G::TM, TN = G::TN, A_BYTES = G::A_BYTES, KSTEPS = G::KSTEPS;
@@ -410,9 +419,16 @@ pipelined_gemm(KArgs args) {
     __shared__ __attribute__((aligned(1024))) char ring3[S > 3 ? G::STAGE : 16];
     __shared__ __attribute__((aligned(1024))) char ring4[S > 4 ? G::STAGE : 16];
     __shared__ __attribute__((aligned(1024))) char ring5[S > 5 ? G::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char ring_a2[LDM == 4 ? G::A_BYTES : 16];
 
-    // ring slot s as a compile-time choice of array (see the header comment)
-    auto slot_of = [&](auto sc) -> SPG_LDS char* {
+    // ring slot s as a compile-time choice of array (see the header comment); a slot
+    // is addressed through its A and B parts, which the A-deep ring (LDM 4) places in
+    // different arrays
+    struct Slot {
+        SPG_LDS char* a;
+        SPG_LDS char* b;
+    };
+    auto ring_of = [&](auto sc) -> SPG_LDS char* {
         constexpr int v = decltype(sc)::value;
         if constexpr (v == 0) return (SPG_LDS char*)ring0;
         else if constexpr (v == 1) return (SPG_LDS char*)ring1;
@@ -420,6 +436,19 @@ pipelined_gemm(KArgs args) {
         else if constexpr (v == 3) return (SPG_LDS char*)ring3;
         else if constexpr (v == 4) return (SPG_LDS char*)ring4;
         else return (SPG_LDS char*)ring5;
+    };
+    auto slot_of = [&](auto sc) -> Slot {
+        SPG_LDS char* r = ring_of(sc);
+        return Slot{r, r + G::A_BYTES};
+    };
+    // slot of k-tile t for t % 6 == i in the A-deep ring: A in the A part of ring0,
+    // ring1 or in ring_a2 (t % 3), B in the B part of ring0 or ring1 (t % 2)
+    auto deep_slot = [&](auto ic) -> Slot {
+        constexpr int i = decltype(ic)::value;
+        SPG_LDS char* a = (i % 3) == 0 ? (SPG_LDS char*)ring0
+                        : (i % 3) == 1 ? (SPG_LDS char*)ring1 : (SPG_LDS char*)ring_a2;
+        SPG_LDS char* b = ((i % 2) == 0 ? (SPG_LDS char*)ring0 : (SPG_LDS char*)ring1) + G::A_BYTES;
+        return Slot{a, b};
     };
 
     const int tid = threadIdx.x;
@@ -539,18 +568,22 @@ pipelined_gemm(KArgs args) {
             else return offB[jb];
         }
     };
-    // op j writes LDS bytes lds_off(j) + 16*lane of the slot
+    // op j writes LDS bytes lds_off(j) + 16*lane of the slot's A part (j < A_DMA) or
+    // B part
     auto lds_off = [&](auto jc) __attribute__((always_inline)) -> int {
         constexpr int j = decltype(jc)::value;
         if constexpr (j < A_DMA) return (wave * A_DMA + j) * 1024;
-        else return A_BYTES + (wave * B_DMA + (j - A_DMA)) * 1024;
+        else return (wave * B_DMA + (j - A_DMA)) * 1024;
+    };
+    auto part = [&](const Slot& slot, auto jc) __attribute__((always_inline)) -> SPG_LDS char* {
+        return decltype(jc)::value < A_DMA ? slot.a : slot.b;
     };
     using NotFirst = std::false_type;
     using First = std::true_type;
-    auto dma_op = [&](SPG_LDS char* slot, const DmaSrc& src, auto jc, auto first)
+    auto dma_op = [&](const Slot& slot, const DmaSrc& src, auto jc, auto first)
                       __attribute__((always_inline)) {
         constexpr int j = decltype(jc)::value;
-        dma16(j < A_DMA ? src.a : src.b, slot + lds_off(jc), src_off(jc, first));
+        dma16(j < A_DMA ? src.a : src.b, part(slot, jc) + lds_off(jc), src_off(jc, first));
     };
     // register staging (LDM 1): one k-tile of copies in flight in VGPRs
     u32x4 stage_regs[G::L];
@@ -559,11 +592,11 @@ pipelined_gemm(KArgs args) {
         stage_regs[j] = __builtin_amdgcn_raw_buffer_load_b128(j < A_DMA ? src.a : src.b,
                                                               (int)src_off(jc, first), 0, 0);
     };
-    auto lwrite_op = [&](SPG_LDS char* slot, auto jc) __attribute__((always_inline)) {
+    auto lwrite_op = [&](const Slot& slot, auto jc) __attribute__((always_inline)) {
         constexpr int j = decltype(jc)::value;
-        *(SPG_LDS u32x4*)(slot + lds_off(jc) + lane * 16) = stage_regs[j];
+        *(SPG_LDS u32x4*)(part(slot, jc) + lds_off(jc) + lane * 16) = stage_regs[j];
     };
-    auto issue = [&](SPG_LDS char* slot, int kt, auto first) __attribute__((always_inline)) {
+    auto issue = [&](const Slot& slot, int kt, auto first) __attribute__((always_inline)) {
         const DmaSrc src = dma_src(kt);
         static_for<0, G::L>([&](auto jc) { dma_op(slot, src, jc, first); });
     };
@@ -630,7 +663,7 @@ pipelined_gemm(KArgs args) {
         for (int kk = 0; kk < KSTEPS; ++kk) {
             const int c = kk * 2 + (lane >> 5);
             const int r = lane & 31;
-            boff[kk] = A_BYTES + (wn * WN + r) * ROWB + (SWZ ? (c ^ kswz_t<BK>(r)) : c) * 16;
+            boff[kk] = (wn * WN + r) * ROWB + (SWZ ? (c ^ kswz_t<BK>(r)) : c) * 16;
         }
     } else {
         // ds_read_b64_tr_b16: in each 16-lane group, lane i supplies 8 B of row
@@ -641,7 +674,7 @@ pipelined_gemm(KArgs args) {
 #pragma unroll
         for (int bn = 0; bn < TN; ++bn) {
             const int chunk = (wn * WN + bn * 32) / 8 + ((lane >> 4) & 1) * 2 + ((lane >> 1) & 1);
-            boff[bn] = A_BYTES + kl * RB + (SWZ ? (chunk ^ nswz(kl)) : chunk) * 16 + (lane & 1) * 8;
+            boff[bn] = kl * RB + (SWZ ? (chunk ^ nswz(kl)) : chunk) * 16 + (lane & 1) * 8;
         }
     }
 
@@ -685,24 +718,24 @@ pipelined_gemm(KArgs args) {
     // the B columns (one ds_read_b128 each for [N,K] storage, two transposing
     // reads -- k 0..3 and 4..7 of the lane's 8 -- for [K,N] storage).
     constexpr int NRD = TM + (B_NK ? TN : 2 * TN);
-    auto read_op = [&](const SPG_LDS char* slot, int kk, Frags& f, auto rc) __attribute__((always_inline)) {
+    auto read_op = [&](const Slot& slot, int kk, Frags& f, auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
         if constexpr (r < TM) {
-            f.a[r] = *(const SPG_LDS u32x4*)(slot + aoff[kk] + r * 32 * ROWB);
+            f.a[r] = *(const SPG_LDS u32x4*)(slot.a + aoff[kk] + r * 32 * ROWB);
         } else if constexpr (B_NK) {
             constexpr int bn = r - TM;
-            f.b[bn] = *(const SPG_LDS u32x4*)(slot + boff[kk] + bn * 32 * ROWB);
+            f.b[bn] = *(const SPG_LDS u32x4*)(slot.b + boff[kk] + bn * 32 * ROWB);
         } else {
             constexpr int bn = (r - TM) / 2, h = (r - TM) % 2;
             constexpr int RB = BN * 2;
             const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (SPG_LDS shortx4*)(slot + boff[bn] + (kk * 16 + h * 4) * RB));
+                (SPG_LDS shortx4*)(slot.b + boff[bn] + (kk * 16 + h * 4) * RB));
             const u32x2 v2 = __builtin_bit_cast(u32x2, v);
             f.b[bn][2 * h] = v2[0];
             f.b[bn][2 * h + 1] = v2[1];
         }
     };
-    auto load_frags = [&](const SPG_LDS char* slot, int kk, Frags& f) __attribute__((always_inline)) {
+    auto load_frags = [&](const Slot& slot, int kk, Frags& f) __attribute__((always_inline)) {
         static_for<0, NRD>([&](auto rc) { read_op(slot, kk, f, rc); });
     };
     auto mma = [&](const Frags& f) __attribute__((always_inline)) {
@@ -723,7 +756,7 @@ pipelined_gemm(KArgs args) {
 #endif
     constexpr int RPS = SPG_READS_PER_STEP;  // LDS reads issued per MFMA step
     constexpr int CPS = G::L / KSTEPS;       // copy ops per stage when spread over a window
-    static_assert(LDM == 0 || G::L % KSTEPS == 0, "copy ops must split evenly over the stages");
+    static_assert(LDM == 0 || LDM == 4 || G::L % KSTEPS == 0, "copy ops must split evenly over the stages");
     // One MFMA stage with its memory traffic interleaved: step i issues MFMA i of
     // `now`, then copy op i and RPS LDS reads of the next stage (into `nx`, from
     // `rslot` at k-step rkk).  Copy modes: 1, all L direct-to-LDS ops of the k-tile
@@ -733,8 +766,8 @@ pipelined_gemm(KArgs args) {
     // after every step keeps this order, so each wave hands the matrix pipe a new
     // MFMA every step while the LDS and the copies are fed in its shadow instead of
     // in bursts.
-    auto stage = [&](const Frags& now, const SPG_LDS char* rslot, int rkk, Frags& nx,
-                     SPG_LDS char* cslot, const auto& src, auto do_read, auto mode, auto j0c)
+    auto stage = [&](const Frags& now, const Slot& rslot, int rkk, Frags& nx,
+                     const Slot& cslot, const auto& src, auto do_read, auto mode, auto j0c)
                      __attribute__((always_inline)) {
         constexpr bool RD = decltype(do_read)::value;
         constexpr int MD = decltype(mode)::value;
@@ -750,8 +783,11 @@ pipelined_gemm(KArgs args) {
                 constexpr int bn = i / TM, bm = i % TM;
                 acc[bn][bm] = mfma<BF16>(now.b[bn], now.a[bm], acc[bn][bm]);
             }
-            if constexpr (MD == 1 && i < NCP)
-                dma_op(cslot, src, std::integral_constant<int, J0 + i>{}, NotFirst{});
+            if constexpr (MD == 1 && i < NCP) {
+                // the A-deep ring issues B before A (see LDM 4)
+                constexpr int j = LDM == 4 ? (J0 + i + A_DMA) % G::L : J0 + i;
+                dma_op(cslot, src, std::integral_constant<int, j>{}, NotFirst{});
+            }
             if constexpr (MD == 2 && i < NCP) {
                 lwrite_op(cslot, std::integral_constant<int, J0 + i>{});
                 gload_op(src, std::integral_constant<int, J0 + i>{}, NotFirst{});
@@ -798,18 +834,19 @@ pipelined_gemm(KArgs args) {
     static_assert(KSTEPS % NF == 0, "fragment sets must tile the k-steps of a k-tile");
     Frags fr[NF];
     auto fset = [&](auto ic) -> Frags& { return fr[decltype(ic)::value % NF]; };
-    using ModeWin = std::integral_constant<int, LDM == 0 ? 1 : (LDM == 1 ? 2 : 3)>;
-    constexpr int WOPS = LDM == 0 ? G::L / PF : CPS;  // copy ops per window stage
-    static_assert(LDM != 0 || G::L % PF == 0, "copies must split over the lookahead stages");
+    constexpr bool DIRECT = LDM == 0 || LDM == 4;     // all copies of a window right after its barrier
+    using ModeWin = std::integral_constant<int, DIRECT ? 1 : (LDM == 1 ? 2 : 3)>;
+    constexpr int WOPS = DIRECT ? G::L / PF : CPS;    // copy ops per window stage
+    static_assert(!DIRECT || G::L % PF == 0, "copies must split over the lookahead stages");
 
     // stage kk of a k-tile: MFMAs of set kk, reads of step kk+PF from `cur` or `nxt`,
     // copies of window position `pos` (if any) from `src` into `cslot`
-    auto kstage = [&](auto kc, const SPG_LDS char* cur, const SPG_LDS char* nxt, SPG_LDS char* cslot,
+    auto kstage = [&](auto kc, const Slot& cur, const Slot& nxt, const Slot& cslot,
                       const auto& src, auto pos, auto do_read) __attribute__((always_inline)) {
         constexpr int kk = decltype(kc)::value;
         constexpr int rk = kk + PF;
         constexpr int P = decltype(pos)::value;          // -1: no copies in this stage
-        const SPG_LDS char* rslot = rk < KSTEPS ? cur : nxt;
+        const Slot& rslot = rk < KSTEPS ? cur : nxt;
         using MD = std::integral_constant<int, P < 0 ? 0 : ModeWin::value>;
         using J = std::integral_constant<int, (P < 0 ? 0 : P) * WOPS>;
         stage(fset(kc), rslot, rk % KSTEPS, fset(std::integral_constant<int, rk>{}), cslot, src,
@@ -818,7 +855,8 @@ pipelined_gemm(KArgs args) {
 
     if constexpr (S == 1) {
         // the serial K loop: copy, wait, multiply, and only then let the next copy in
-        SPG_LDS char* r0 = slot_of(Z_{});
+        const Slot r0 = slot_of(Z_{});
+        const Slot none{nullptr, nullptr};
         issue(r0, 0, First{});
         for (int t = 0; t < nk; ++t) {
             wait_vmcnt<0>();
@@ -827,7 +865,7 @@ pipelined_gemm(KArgs args) {
             static_for<0, KSTEPS>([&](auto kc) {
                 constexpr int kk = decltype(kc)::value;
                 using RD = std::integral_constant<bool, kk + 1 < KSTEPS>;
-                kstage(kc, r0, nullptr, nullptr, kNoCopy, std::integral_constant<int, -1>{}, RD{});
+                kstage(kc, r0, none, none, kNoCopy, std::integral_constant<int, -1>{}, RD{});
             });
             __syncthreads();
             issue(r0, t + 1, NotFirst{});  // past the last k-tile: zeros
@@ -838,7 +876,7 @@ pipelined_gemm(KArgs args) {
         // needs no branches.
         const int nt = ((nk + S - 1) / S) * S;
         auto first_of = [](auto sc) { return std::integral_constant<bool, decltype(sc)::value == 0>{}; };
-        constexpr int PRE = LDM == 0 ? 0 : PF * CPS;  // ops of k-tile S-1 the window before k-tile 0 moves
+        constexpr int PRE = DIRECT ? 0 : PF * CPS;  // ops of k-tile S-1 the window before k-tile 0 moves
         if constexpr (PERS) {
             // prologue: the first S k-tiles of the stream fill every slot
             static_for<0, S>([&](auto sc) {
@@ -846,6 +884,15 @@ pipelined_gemm(KArgs args) {
                 static_for<0, G::L>([&](auto jc) { dma_op(slot_of(sc), src, jc, NotFirst{}); });
             });
             wait_vmcnt<(S - 1) * G::L>();
+        } else if constexpr (LDM == 4) {
+            // prologue: k-tiles 0 and 1, and A of k-tile 2; wait for k-tile 0
+            issue(deep_slot(Z_{}), 0, First{});
+            issue(deep_slot(std::integral_constant<int, 1>{}), 1, NotFirst{});
+            const DmaSrc src = dma_src(2);
+            static_for<0, A_DMA>([&](auto jc) {
+                dma_op(deep_slot(std::integral_constant<int, 2>{}), src, jc, NotFirst{});
+            });
+            wait_vmcnt<G::L + A_DMA>();
         } else if constexpr (LDM == 0) {
             // prologue: k-tiles 0 .. S-1 fill every slot; wait for k-tile 0
             static_for<0, S>([&](auto sc) { issue(slot_of(sc), sc.value, first_of(sc)); });
@@ -877,17 +924,25 @@ pipelined_gemm(KArgs args) {
         lds_barrier();
         static_for<0, PF>([&](auto kc) { load_frags(slot_of(Z_{}), kc.value, fset(kc)); });
 
-        constexpr int STEADY = (S - 2) * G::L;
+        // outstanding copies allowed at the wait before barrier t: k-tiles t+2 .. t+S-1
+        // (and, in the A-deep ring, A of k-tile t+2)
+        constexpr int STEADY = LDM == 4 ? A_DMA : (S - 2) * G::L;
         auto ktile = [&](auto sc, int t) __attribute__((always_inline)) {
             constexpr int s = decltype(sc)::value;
-            SPG_LDS char* cur = slot_of(sc);
-            SPG_LDS char* prev = slot_of(std::integral_constant<int, (s + S - 1) % S>{});
-            const SPG_LDS char* nxt = slot_of(std::integral_constant<int, (s + 1) % S>{});
+            // slots of k-tiles t-1, t, t+1 (s = t mod S, or t mod 6 in the A-deep ring)
+            auto slot_at = [&](auto ic) -> Slot {
+                if constexpr (LDM == 4) return deep_slot(std::integral_constant<int, decltype(ic)::value % 6>{});
+                else return slot_of(std::integral_constant<int, decltype(ic)::value % S>{});
+            };
+            constexpr int NS = LDM == 4 ? 6 : S;
+            const Slot cur = slot_at(sc);
+            const Slot prev = slot_at(std::integral_constant<int, (s + NS - 1) % NS>{});
+            const Slot nxt = slot_at(std::integral_constant<int, (s + 1) % NS>{});
             auto src_of = [&](int kt) __attribute__((always_inline)) {
                 if constexpr (LDM == 1) return reg_src(kt);
                 else return dma_src(kt);
             };
-            if constexpr (LDM == 0) {
+            if constexpr (DIRECT) {
                 // all copies of a window are issued right after its barrier
                 static_for<0, KSTEPS - PF>([&](auto kc) {
                     kstage(kc, cur, nxt, prev, kNoCopy, std::integral_constant<int, -1>{}, T_{});
@@ -916,6 +971,7 @@ pipelined_gemm(KArgs args) {
                 // (register staging: write k-tile t+S, load k-tile t+S+1)
                 const auto src = [&]() __attribute__((always_inline)) {
                     if constexpr (PERS) return next_copy();
+                    else if constexpr (LDM == 4) return DmaSrc{dma_src(t + 3).a, dma_src(t + 2).b};
                     else return src_of(LDM == 1 ? t + S + 1 : t + S);
                 }();
                 static_for<KSTEPS - PF, KSTEPS>([&](auto kc) {
@@ -948,6 +1004,17 @@ pipelined_gemm(KArgs args) {
             for (int t0 = 0; t0 < ns; t0 += S) {
                 static_for<0, S>([&](auto sc) { ktile(sc, t0 + decltype(sc)::value); });
             }
+        } else if constexpr (LDM == 4) {
+            // six k-tiles per iteration (the slot pattern repeats every 6), then the
+            // remaining nk % 6 one by one: no k-tile past nk is multiplied
+            int t0 = 0;
+            for (; t0 + 6 <= nk; t0 += 6) {
+                static_for<0, 6>([&](auto sc) { ktile(sc, t0 + decltype(sc)::value); });
+            }
+            const int rem = nk - t0;
+            static_for<0, 5>([&](auto sc) {
+                if (decltype(sc)::value < rem) ktile(sc, t0 + decltype(sc)::value);
+            });
         } else {
             for (int t0 = 0; t0 < nt; t0 += S) {
                 static_for<0, S>([&](auto sc) { ktile(sc, t0 + decltype(sc)::value); });

@@ -28,4 +28,5 @@
 #define SPG_V_21(...)
 #define SPG_V_22(...)
 #define SPG_V_23(...)
+#define SPG_V_24(...)
 #include "variants.inc"

@@ -28,4 +28,5 @@
 #define SPG_V_21(...)
 #define SPG_V_22(...) SPG_INSTANTIATE_ALL(__VA_ARGS__)
 #define SPG_V_23(...)
+#define SPG_V_24(...)
 #include "variants.inc"

@@ -236,6 +236,30 @@ def test_persistent_falls_back_where_it_does_not_apply():
         assert np.array_equal(G.c_values(C2, w), got)
 
 
+def test_a_deep_ring_every_tail():
+    # the A-deep ring runs six k-tiles per iteration and then the rest one by one: every
+    # remainder 0..5, fewer k-tiles than one iteration, a leading partial k-tile, both
+    # layouts; bitwise equal to the two-deep ring (same k order) and within tolerance
+    deep = [c for c in _variants() if c.staging == 4]
+    assert deep, "no A-deep configuration compiled"
+    d = deep[0]
+    twin = [c for c in _variants() if c.staging == 0 and (c.block_m, c.block_n, c.block_k, c.stages,
+            c.wave_m, c.wave_n, c.lookahead, c.schedule, c.persistent) ==
+            (d.block_m, d.block_n, d.block_k, d.stages, d.wave_m, d.wave_n, d.lookahead, d.schedule,
+             d.persistent)][0]
+    for K in (40, 64, 128, 192, 256, 320, 384, 448, 760, 1024):
+        for layout in (W.B_KN, W.B_NK):
+            w = W.custom(300, 520, K, W.BF16, W.BF16, layout, "none", ("uniform", -1.0, 1.0))
+            a, b = W.make_inputs(w)
+            _log(f"a-deep K={K} {w.describe()}")
+            C, used = G.run(w, a, b, force=d)
+            assert used.staging == 4
+            got = G.c_values(C, w)
+            G.check(w, a, b, got)
+            C2, _ = G.run(w, a, b, force=twin)
+            assert np.array_equal(G.c_values(C2, w), got)
+
+
 def test_autotune_keeps_parity():
     w = W.custom(1024, 768, 512, W.F16, W.F16, W.B_NK)
     a, b = W.make_inputs(w)
