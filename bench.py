@@ -246,7 +246,7 @@ def kernel_name(w, cfg) -> str:
     """The template instantiation a configuration launches (as profilers print it)."""
     b = lambda v: "true" if v else "false"
     # the persistent instantiation runs only on the shapes it takes (else its twin)
-    pers = (cfg.persistent and w.out_dtype != "f32" and w.K % cfg.block_k == 0
+    pers = (cfg.persistent and not cfg.store and w.out_dtype != "f32" and w.K % cfg.block_k == 0
             and (w.b_layout == "nk" or w.N % cfg.block_n == 0))
     return (f"spg::pipelined_gemm<{b(w.in_dtype == 'bf16')}, {b(w.b_layout == 'nk')}, "
             f"{cfg.block_m}, {cfg.block_n}, {cfg.block_k}, {cfg.wave_m}, {cfg.wave_n}, "
@@ -275,7 +275,8 @@ def measured_traffic(workload: str, cfg, w):
 
 
 def parse_tile(spec):
-    """'256x256x64:2[:swizzle[:group_m[:staging[:WMxWN[:lookahead[:schedule[:persistent]]]]]]]' -> the matching
+    """'256x256x64:2[:swizzle[:group_m[:staging[:WMxWN[:lookahead[:schedule[:persistent[:store[:xcd_remap]]]]]]]]]'
+    -> the matching
     compiled configuration (the first one in the table when the wave tile is not given)."""
     import software_pipelined_tiled_gemm_amd as spg
 
@@ -291,6 +292,8 @@ def parse_tile(spec):
     look = int(parts[6]) if len(parts) > 6 else 1
     sched = int(parts[7]) if len(parts) > 7 else 0
     pers = int(parts[8]) if len(parts) > 8 else 0
+    store = int(parts[9]) if len(parts) > 9 else 0
+    xcd = int(parts[10]) if len(parts) > 10 else 1
     for i in range(spg.gemm_num_configs()):
         c = spg.gemm_list_config(i)
         if wave is not None and (c.wave_m, c.wave_n) != wave:
@@ -300,6 +303,8 @@ def parse_tile(spec):
         if (c.block_m, c.block_n, c.block_k, c.stages, c.swizzle, c.staging) == (bm, bn, bk, st, swz, stg):
             if gm:
                 c.group_m = gm
+            c.store = store
+            c.xcd_remap = xcd
             return c
     raise SystemExit(f"no compiled configuration matches --tile {spec}")
 
@@ -322,6 +327,14 @@ ABLATIONS = [
     ("256x128 tile, wave-specialized (producer wave + 4 consumers)", "256x128x64:3:1:8:3:128x64:1:0"),
     ("128x128 tile, 4 waves of 64x64, S=3", "128x128x64:3:1:8:0:64x64:1:0"),
     ("persistent: one workgroup per CU, its tiles as one k-tile stream", "256x256x64:2:1:8:0:128x64:1:0:1"),
+    ("epilogue stored from registers (no LDS staging)", "256x256x64:2:1:8:4:128x64:1:0:0:1"),
+    ("no tile remap (row-major raster, no XCD ranges)", "256x256x64:2:1:1:4:128x64:1:0:0:0:0"),
+    ("XCD ranges only (group_m 1)", "256x256x64:2:1:1:4:128x64:1:0:0:0:1"),
+    ("raster groups only (group_m 8, no XCD ranges)", "256x256x64:2:1:8:4:128x64:1:0:0:0:0"),
+    ("128x128 tile, 4 waves of 64x64, S=2", "128x128x64:2:1:8:0:64x64:1:0"),
+    ("128x128 tile, 4 waves of 64x64, S=4", "128x128x64:4:1:8:0:64x64:1:0"),
+    ("128x128 tile, S=3, release delay 1 (S-1 in flight)", "128x128x64:3:1:8:5:64x64:1:0"),
+    ("256x128 tile, 8 waves of 64x64, S=3, release delay 1", "256x128x64:3:1:8:5:64x64:1:0"),
 ]
 
 
@@ -348,7 +361,7 @@ def main():
     ap.add_argument("--workload", default="nn_bf16_8192",
                     help="workload name from workloads.WORKLOADS")
     ap.add_argument("--tile", default=None,
-                    help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging[:WMxWN[:lookahead[:schedule[:persistent]]]]]]] "
+                    help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging[:WMxWN[:lookahead[:schedule[:persistent[:store[:xcd_remap]]]]]]]]] "
                          "(default: the library's choice)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra lines (fp16 8192^3, the 8-GPU shard, the standalone "

@@ -20,7 +20,9 @@
  *     B is [K,N] (GEMM_B_KN, leading dimension N) or [N,K] (GEMM_B_NK,
  *     leading dimension K).  C is [M,N] (leading dimension N).
  *   - A, B and C are device pointers owned by the caller; the library never
- *     frees or retains them.  C must not overlap A or B (not checked).
+ *     frees or retains them.  C must not overlap A or B (not checked).  The
+ *     pipelined kernel needs A, B and C 16-byte aligned; other pointers run the
+ *     simple kernel.
  *   - Out-of-range elements of partial tiles contribute exactly zero and are
  *     never written: any M, N, K >= 0 is accepted.  M == 0 or N == 0 is a no-op;
  *     K == 0 writes epi(0) = 0 everywhere.
@@ -83,7 +85,10 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1, GEMM_EPI_RELU = 2 } ge
  *                       counters in LDS replace the barrier;
  *                       4 = as 0, with A in a ring one slot deeper than B (stages =
  *                       2: three A slots, two B slots), so the copies of A have two
- *                       k-tiles to land and those of B one
+ *                       k-tiles to land and those of B one;
+ *                       5 = as 0, with a slot refilled one k-tile after its release
+ *                       (the Pallas guide's release delay of 1; stages >= 3): S-1
+ *                       k-tiles in flight instead of S
  *   lookahead           MFMA k-steps between the LDS read of an operand fragment and
  *                       its use: 1 (two fragment sets in registers) or 2 (four sets;
  *                       block_k 64, stages >= 2)
@@ -101,6 +106,12 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1, GEMM_EPI_RELU = 2 } ge
  *                       K % block_k == 0, the output is fp16/bf16 and, for GEMM_B_KN,
  *                       N % block_n == 0; other problems run the same tile with one
  *                       workgroup per tile.  0 = one workgroup per tile.
+ *   store               0 = the epilogue stages each wave's output through LDS and
+ *                       writes 16-byte row segments (default); 1 = for fp16/bf16
+ *                       output, each lane stores its own accumulator values straight
+ *                       from registers (4 consecutive outputs per store; the ablation
+ *                       of the staging).  fp32 output and the persistent and
+ *                       wave-specialized modes always stage.
  * The LDS a configuration needs is stages * (block_m + block_n) * block_k * 2 bytes
  * (the shared-memory bound of the TileLang tutorial's shared_bytes()), plus
  * block_m * block_k * 2 for staging 4, at most 160 KiB. */
@@ -115,6 +126,7 @@ typedef struct {
     int32_t lookahead;
     int32_t schedule;
     int32_t persistent;
+    int32_t store;
 } gemm_tile_config;
 
 typedef struct gemm_plan* gemm_handle;

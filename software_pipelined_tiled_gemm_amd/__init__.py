@@ -25,7 +25,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "out of memory",
 DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
 B_LAYOUTS = {"kn": 0, "nk": 1}
 EPILOGUES = {"none": 0, "gelu_tanh": 1, "relu": 2}
-STAGING = {0: "direct", 1: "vgpr", 2: "direct-spread", 3: "producer-wave", 4: "direct-a-deep"}
+STAGING = {0: "direct", 1: "vgpr", 2: "direct-spread", 3: "producer-wave", 4: "direct-a-deep",
+           5: "direct-late-release"}
 
 
 class GemmError(RuntimeError):
@@ -41,7 +42,7 @@ class TileConfig(ctypes.Structure):
                 ("swizzle", ctypes.c_int32), ("group_m", ctypes.c_int32),
                 ("xcd_remap", ctypes.c_int32), ("staging", ctypes.c_int32),
                 ("lookahead", ctypes.c_int32), ("schedule", ctypes.c_int32),
-                ("persistent", ctypes.c_int32)]
+                ("persistent", ctypes.c_int32), ("store", ctypes.c_int32)]
 
     def __init__(self, **kw):
         kw.setdefault("lookahead", 1)
@@ -64,7 +65,7 @@ class TileConfig(ctypes.Structure):
                 f"group_m={d['group_m']}, xcd_remap={d['xcd_remap']}, "
                 f"staging={STAGING.get(d['staging'], d['staging'])}, lookahead={d['lookahead']}, "
                 f"schedule={'compiler' if d['schedule'] else 'manual'}"
-                f"{', persistent' if d['persistent'] else ''})")
+                f"{', persistent' if d['persistent'] else ''}{', direct store' if d['store'] else ''})")
 
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_get_config", "gemm_autotune",

@@ -199,6 +199,7 @@ KArgs make_args(const gemm_plan* p, const void* A, const void* B, void* C, int b
     a.out_dtype = (int32_t)p->out;
     a.epilogue = (int32_t)p->epi;
     a.persistent = 0;
+    a.store_direct = p->cfg.store ? 1 : 0;
     return a;
 }
 
@@ -216,7 +217,8 @@ gemm_status launch_plan(const gemm_plan* p, const gemm_tile_config& cfg, const V
                         const void* A, const void* B, void* C, hipStream_t st) {
     const bool bf = p->in == GEMM_BF16;
     const bool nk = p->bl == GEMM_B_NK;
-    const bool aligned = ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0);
+    // 16-byte copies from A and B, 16-byte stores to C
+    const bool aligned = ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && ((uintptr_t)C % 16 == 0);
     if (p->simple || !aligned || var == nullptr) {
         gemm_plan q = *p;
         q.cfg.group_m = 1;
@@ -229,7 +231,7 @@ gemm_status launch_plan(const gemm_plan* p, const gemm_tile_config& cfg, const V
         q.cfg = cfg;
         KArgs a = make_args(&q, A, B, C, cfg.block_m, cfg.block_n);
         int64_t wgs = (int64_t)a.tiles_m * a.tiles_n;
-        if (persistent_fits(p, cfg)) {
+        if (persistent_fits(p, cfg) && !cfg.store) {
             // one workgroup per CU (its LDS allows no second), each walking its tiles
             const int cus = cu_count();
             if (cus > 0) {
@@ -297,7 +299,8 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
             force->stages <= 0 || force->wave_m <= 0 || force->wave_n <= 0 ||
             force->group_m < 0 || (force->swizzle != 0 && force->swizzle != 1) ||
             (force->xcd_remap != 0 && force->xcd_remap != 1) ||
-            force->staging < 0 || force->staging > 4 ||
+            force->staging < 0 || force->staging > 5 ||
+            (force->store != 0 && force->store != 1) ||
             (force->lookahead != 1 && force->lookahead != 2) ||
             (force->schedule != 0 && force->schedule != 1) ||
             (force->persistent != 0 && force->persistent != 1))

@@ -86,6 +86,7 @@ struct KArgs {
     int32_t out_dtype;
     int32_t epilogue;
     int32_t persistent;   // launcher only: run the persistent instantiation (grid = CUs)
+    int32_t store_direct; // 1: the epilogue stores from registers, without LDS staging
 };
 
 // ---------------------------------------------------------------------------
@@ -153,8 +154,13 @@ __device__ __forceinline__ float gelu_tanh(float x) {
     // 0.5 x (1 + tanh(u)) == x * sigmoid(2u) == x / (1 + exp(-2u)),
     // u = 0.7978845608 (x + 0.044715 x^3).  exp via v_exp_f32 (2^x); the
     // form saturates cleanly: exp -> inf gives -0, exp -> 0 gives x.
-    float u = 0.7978845608f * (x + 0.044715f * x * x * x);
-    float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * u);  // 2*log2(e) = 2.885...
+    // The one fused multiply-add is written out and contraction is off otherwise, so
+    // every inlined copy (the staged and the direct epilogue, the standalone kernel)
+    // rounds the same way and gives the same bits.
+#pragma clang fp contract(off)
+    const float x3 = 0.044715f * x * x;
+    const float u = 0.7978845608f * __builtin_fmaf(x3, x, x);
+    const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * u);  // 2*log2(e) = 2.885...
     return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
@@ -175,6 +181,10 @@ __device__ __forceinline__ float epi_apply(float x, int epi) {
 
 __device__ __forceinline__ uint16_t f32_to_bits(float x, bool bf16) {
     if (bf16) return __builtin_bit_cast(uint16_t, (__bf16)x);   // v_cvt_pk_bf16_f32, RNE
+    // Without the empty asm the compiler may fold a preceding multiply into the
+    // conversion (v_fma_mixlo_f16 a, b, 0): one rounding instead of two, and a -0
+    // product comes out +0, so the bits would depend on the code around the call.
+    asm("" : "+v"(x));
     return __builtin_bit_cast(uint16_t, (_Float16)x);            // v_cvt_f16_f32, RNE
 }
 
@@ -303,6 +313,46 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TN][TM], char* 
     }
 }
 
+// Epilogue without LDS staging (the ablation of the staged one), 16-bit outputs: each
+// lane stores its own accumulator values, 4 consecutive outputs of one row per store,
+// so one wave instruction writes 32 rows x 2 segments of 8 bytes.  The epilogue and the
+// output type are applied per value at run time: one instantiation per kernel.
+template <int TM, int TN>
+__device__ __forceinline__ void store_direct16(const floatx16 (&acc)[TN][TM], const KArgs& args,
+                                               int m_base, int n_base, int lane) {
+    const int M = args.M, N = args.N;
+    const int ep = args.epilogue;
+    const bool bf = args.out_dtype == kOutBF16;
+    const bool vec_ok = (N % 4) == 0;    // then every 4-output segment is 8-byte aligned
+#pragma unroll
+    for (int bm = 0; bm < TM; ++bm) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int gm = m_base + bm * 32 + (lane & 31);
+#pragma unroll
+        for (int bn = 0; bn < TN; ++bn) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = epi_apply(acc[bn][bm][4 * q + e], ep);
+                    h[e] = bf ? (uint32_t)f32_to_bits(x, true) : (uint32_t)f32_to_bits(x, false);
+                }
+                const int gn = n_base + bn * 32 + 8 * q + 4 * (lane >> 5);
+                if (gm < M && gn < N) {
+                    uint16_t* dst = (uint16_t*)args.C + ((size_t)gm * N + gn);
+                    if (vec_ok && gn + 4 <= N) {
+                        *(u32x2*)dst = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+                    } else {
+                        const int lim = (N - gn) < 4 ? (N - gn) : 4;
+                        for (int e = 0; e < lim; ++e) dst[e] = (uint16_t)h[e];
+                    }
+                }
+            }
+        }
+    }
+}
+
 // Largest number of 32-row blocks (a divisor of TM) whose staging fits `budget` bytes.
 template <int TM, int WN, int OB>
 constexpr int blocks_per_round(int budget) {
@@ -375,6 +425,12 @@ __device__ __forceinline__ int kswz_t(int r) {
 //      A copies of k-tile t+3 in flight.  With the tile raster's 8 x 4 blocks of
 //      tiles per XCD, A carries 2/3 of the bytes that miss L2.  The loop is unrolled
 //      by 6 k-tiles (three A slots x two B slots), plus an unrolled tail.
+//   5  direct-to-LDS copies as in 0, but a slot is refilled one k-tile after its
+//      release (the release delay of 1 in the Pallas guide's terms): the window
+//      after barrier t copies k-tile t+S-1 into the slot released at barrier t-1, so
+//      S-1 k-tiles are in flight instead of S (needs S >= 3).  Mode 0 refills a slot
+//      at the barrier that releases it, which is the same barrier that publishes the
+//      next k-tile: no second barrier is needed for the early release.
 //
 // PF (lookahead) is the number of MFMA k-steps between the LDS read of an operand
 // fragment and its use: 1 keeps two fragment sets in registers, 2 keeps four and
@@ -405,6 +461,7 @@ pipelined_gemm(KArgs args) {
     static_assert(!PERS || (LDM == 0 && S >= 2), "persistent: direct copies and a ring of >= 2 slots");
     static_assert(LDM != 4 || (S == 2 && S * G::STAGE + G::A_BYTES <= 160 * 1024),
                   "A-deep ring: two slots plus one more A slot within the LDS");
+    static_assert(LDM != 5 || S >= 3, "a late release needs a ring of three slots or more");
     static_assert(!PERS || S * G::STAGE + G::NW * 32 * WN * 2 <= 160 * 1024,
                   "persistent: ring + epilogue staging must fit the LDS");
     constexpr int TM = G::TM, TN = G::TN, A_BYTES = G::A_BYTES, KSTEPS = G::KSTEPS;
@@ -756,7 +813,7 @@ pipelined_gemm(KArgs args) {
 #endif
     constexpr int RPS = SPG_READS_PER_STEP;  // LDS reads issued per MFMA step
     constexpr int CPS = G::L / KSTEPS;       // copy ops per stage when spread over a window
-    static_assert(LDM == 0 || LDM == 4 || G::L % KSTEPS == 0, "copy ops must split evenly over the stages");
+    static_assert(LDM == 0 || LDM == 4 || LDM == 5 || G::L % KSTEPS == 0, "copy ops must split evenly over the stages");
     // One MFMA stage with its memory traffic interleaved: step i issues MFMA i of
     // `now`, then copy op i and RPS LDS reads of the next stage (into `nx`, from
     // `rslot` at k-step rkk).  Copy modes: 1, all L direct-to-LDS ops of the k-tile
@@ -834,7 +891,7 @@ pipelined_gemm(KArgs args) {
     static_assert(KSTEPS % NF == 0, "fragment sets must tile the k-steps of a k-tile");
     Frags fr[NF];
     auto fset = [&](auto ic) -> Frags& { return fr[decltype(ic)::value % NF]; };
-    constexpr bool DIRECT = LDM == 0 || LDM == 4;     // all copies of a window right after its barrier
+    constexpr bool DIRECT = LDM == 0 || LDM == 4 || LDM == 5;  // all copies of a window right after its barrier
     using ModeWin = std::integral_constant<int, DIRECT ? 1 : (LDM == 1 ? 2 : 3)>;
     constexpr int WOPS = DIRECT ? G::L / PF : CPS;    // copy ops per window stage
     static_assert(!DIRECT || G::L % PF == 0, "copies must split over the lookahead stages");
@@ -893,6 +950,11 @@ pipelined_gemm(KArgs args) {
                 dma_op(deep_slot(std::integral_constant<int, 2>{}), src, jc, NotFirst{});
             });
             wait_vmcnt<G::L + A_DMA>();
+        } else if constexpr (LDM == 5) {
+            // prologue: k-tiles 0 .. S-2 (slot S-1 is filled by the first window); wait
+            // for k-tile 0
+            static_for<0, S - 1>([&](auto sc) { issue(slot_of(sc), sc.value, first_of(sc)); });
+            wait_vmcnt<(S - 2) * G::L>();
         } else if constexpr (LDM == 0) {
             // prologue: k-tiles 0 .. S-1 fill every slot; wait for k-tile 0
             static_for<0, S>([&](auto sc) { issue(slot_of(sc), sc.value, first_of(sc)); });
@@ -926,7 +988,7 @@ pipelined_gemm(KArgs args) {
 
         // outstanding copies allowed at the wait before barrier t: k-tiles t+2 .. t+S-1
         // (and, in the A-deep ring, A of k-tile t+2)
-        constexpr int STEADY = LDM == 4 ? A_DMA : (S - 2) * G::L;
+        constexpr int STEADY = LDM == 4 ? A_DMA : (LDM == 5 ? (S - 3) * G::L : (S - 2) * G::L);
         auto ktile = [&](auto sc, int t) __attribute__((always_inline)) {
             constexpr int s = decltype(sc)::value;
             // slots of k-tiles t-1, t, t+1 (s = t mod S, or t mod 6 in the A-deep ring)
@@ -972,12 +1034,16 @@ pipelined_gemm(KArgs args) {
                 const auto src = [&]() __attribute__((always_inline)) {
                     if constexpr (PERS) return next_copy();
                     else if constexpr (LDM == 4) return DmaSrc{dma_src(t + 3).a, dma_src(t + 2).b};
+                    else if constexpr (LDM == 5) return dma_src(t + S - 1);
                     else return src_of(LDM == 1 ? t + S + 1 : t + S);
                 }();
+                // the slot refilled: the one released here, or (release delay 1) the one
+                // released at the previous barrier
+                const Slot fill = LDM == 5 ? prev : cur;
                 static_for<KSTEPS - PF, KSTEPS>([&](auto kc) {
                     constexpr int kk = decltype(kc)::value;
                     using Pos = std::integral_constant<int, kk - (KSTEPS - PF)>;
-                    kstage(kc, cur, nxt, cur, src, Pos{}, T_{});
+                    kstage(kc, cur, nxt, fill, src, Pos{}, T_{});
                 });
             }
             __builtin_amdgcn_s_setprio(0);
@@ -1031,6 +1097,10 @@ pipelined_gemm(KArgs args) {
         // the loop leaves zero-fill copies of k-tiles >= nt in flight: let them land
         // before the ring is reused for staging
         wait_vmcnt<0>();
+        if (args.store_direct && args.out_dtype != kOutF32) {
+            store_direct16<TM, TN>(acc, args, m0 + wm * WM, n0 + wn * WN, lane);
+            return;
+        }
         __syncthreads();  // the ring is drained and free for staging
         char* stg;
         {

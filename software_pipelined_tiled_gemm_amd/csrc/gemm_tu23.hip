@@ -29,4 +29,5 @@
 #define SPG_V_22(...)
 #define SPG_V_23(...) SPG_INSTANTIATE_ALL(__VA_ARGS__)
 #define SPG_V_24(...)
+#define SPG_V_25(...)
 #include "variants.inc"

@@ -126,6 +126,18 @@ def test_forced_configs(L):
         spg.gemm_create(512, 512, 512, force=per)
     assert e.value.status == 1
     assert any(spg.gemm_list_config(i).persistent for i in range(n))
+    sto = spg.TileConfig(block_m=256, block_n=256, block_k=64, stages=2, wave_m=128,
+                         wave_n=64, swizzle=1, group_m=4, xcd_remap=1, store=2)
+    with pytest.raises(spg.GemmError) as e:
+        spg.gemm_create(512, 512, 512, force=sto)
+    assert e.value.status == 1
+    # release delay 1 (staging 5) needs a ring of three slots; the A-deep ring (staging 4)
+    # holds one more k-tile of A than the TileLang budget formula counts
+    for i in range(n):
+        c = spg.gemm_list_config(i)
+        assert c.staging != 5 or c.stages >= 3
+        if c.staging == 4:
+            assert spg.gemm_lds_bytes(c) == (c.stages * (c.block_m + c.block_n) + c.block_m) * c.block_k * 2
     for look in (0, 3):
         far = spg.TileConfig(block_m=256, block_n=256, block_k=64, stages=2, wave_m=128,
                              wave_n=128, swizzle=1, group_m=4, xcd_remap=1, lookahead=look)

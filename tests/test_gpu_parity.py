@@ -142,6 +142,45 @@ def test_misaligned_pointers_take_the_simple_path():
     G.check(w, a, b, G.c_values(C, w))
 
 
+def test_misaligned_output_takes_the_simple_path():
+    import torch
+    w = W.custom(100, 72, 64, W.BF16, W.BF16, W.B_KN)
+    a, b = W.make_inputs(w)
+    A, B = G.to_dev(a), G.to_dev(b)
+    big = torch.zeros(w.M * w.N + 1, dtype=torch.int16, device=G.torch_dev())
+    C = big[1:].view(w.M, w.N)                     # 2-byte aligned
+    with spg.Gemm(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.b_layout) as g:
+        g(A, B, C)
+    torch.cuda.synchronize()
+    assert int(big[0]) == 0
+    G.check(w, a, b, G.c_values(C, w))
+
+
+@pytest.mark.parametrize("out_dtype", [W.F16, W.BF16, W.F32])
+def test_direct_store_epilogue(out_dtype):
+    # the epilogue stored from registers (the ablation of LDS staging): same values as the
+    # staged one, masked edges, N % 4 != 0 element stores; fp32 output keeps the staging
+    picks = [c for c in _variants() if c.staging == 0 and c.persistent == 0 and c.schedule == 0
+             and c.lookahead == 1 and c.swizzle == 1 and c.stages >= 2
+             and (c.block_m, c.block_n, c.wave_m, c.wave_n) in ((256, 256, 128, 64), (128, 128, 64, 64))]
+    one_per_tile = {}
+    for c in picks:
+        one_per_tile.setdefault((c.block_m, c.block_n), c)
+    assert len(one_per_tile) == 2
+    for base in one_per_tile.values():
+        for (M, N, K, epi) in ((300, 520, 200, "gelu_tanh"), (257, 262, 64, "relu"), (512, 512, 128, "none")):
+            w = W.custom(M, N, K, W.F16, out_dtype, W.B_NK, epi, ("uniform", -1.0, 1.0))
+            a, b = W.make_inputs(w)
+            d = spg.TileConfig.from_dict(dict(base.as_dict(), store=1))
+            _log(f"direct store {d} {w.describe()}")
+            C, used = G.run(w, a, b, force=d)
+            assert used.store == 1
+            got = G.c_values(C, w)
+            G.check(w, a, b, got)
+            C2, _ = G.run(w, a, b, force=base)
+            assert np.array_equal(G.c_values(C2, w), got)
+
+
 def test_deterministic_and_untouched_outside():
     import torch
     w = W.custom(300, 200, 256, W.BF16, W.BF16, W.B_KN)
