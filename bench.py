@@ -140,9 +140,38 @@ def gelu_lines(steps, warmup):
     return out
 
 
-def sustained_clock(w, seconds=2.0):
-    """Runs the workload back to back for `seconds` while sampling the engine clock the
-    SMU reports (rocm-smi); returns (median MHz, kernel us at that time) or None."""
+def _socket_power_w():
+    """Socket power the SMU reports (amd-smi metric -p), or None."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p"], capture_output=True, text=True, timeout=10)
+        m = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", r.stdout)
+        return float(m.group(1)) if m else None
+    except Exception:
+        return None
+
+
+def _power_cap_w():
+    """The package power limit (rocm-smi --showmaxpower), or None."""
+    import json as _json
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showmaxpower", "--json"], capture_output=True, text=True,
+                           timeout=10)
+        for card in _json.loads(r.stdout).values():
+            v = card.get("Max Graphics Package Power (W)")
+            if v is not None:
+                return float(v)
+    except Exception:
+        pass
+    return None
+
+
+def sustained_clock(w, seconds=3.0):
+    """Runs the workload back to back for `seconds` while sampling the engine clock
+    (rocm-smi) and the socket power (amd-smi) the SMU reports; returns (median MHz,
+    kernel us at that time, median socket W or None) or None."""
     import json as _json
     import subprocess
     import threading
@@ -159,7 +188,7 @@ def sustained_clock(w, seconds=2.0):
     B = torch.from_numpy(b.view(np.int16)).to(dev)
     C = torch.empty((w.M, w.N), dtype=torch.int16 if w.out_dtype != W.F32 else torch.float32,
                     device=dev)
-    samples, stop = [], threading.Event()
+    samples, watts, stop = [], [], threading.Event()
 
     def sample():
         while not stop.is_set():
@@ -172,6 +201,9 @@ def sustained_clock(w, seconds=2.0):
                         samples.append(float(v.strip("()Mhz")))
             except Exception:
                 return
+            p = _socket_power_w()
+            if p is not None:
+                watts.append(p)
             time.sleep(0.2)
 
     g = spg.Gemm(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.b_layout, w.epilogue)
@@ -198,7 +230,8 @@ def sustained_clock(w, seconds=2.0):
     if len(samples) < 3:
         return None
     samples = sorted(samples[1:])
-    return samples[len(samples) // 2], us
+    watts = sorted(watts[1:])
+    return samples[len(samples) // 2], us, (watts[len(watts) // 2] if watts else None)
 
 
 def cpu_baseline(w, target_s=15.0):
@@ -418,12 +451,14 @@ def main():
         log(f"  fused vs unfused GELU GEMM: {extra['gemm_gelu_3072x4096x4096']}")
         clk = sustained_clock(w)
         if clk is not None:
-            mhz, us = clk
+            mhz, us, watts = clk
             tf = w.flops / (us * 1e-6) / 1e12
             extra["sustained_clock"] = {
                 "sclk_mhz_median": mhz, "kernel_us": round(us, 2), "tflops": round(tf, 2),
                 "mfma_busy_at_that_clock": round(tf / (PEAK_TFLOPS[w.in_dtype] * mhz / 2400.0), 4),
-                "note": "2 s back-to-back run, clock sampled with rocm-smi; peak scales with clock"}
+                "socket_power_w_median": watts, "package_power_cap_w": _power_cap_w(),
+                "note": "3 s back-to-back run; clock (rocm-smi) and socket power (amd-smi) sampled "
+                        "while it runs; peak scales with clock"}
             log(f"  sustained: {extra['sustained_clock']}")
 
     if args.copy_calibration:
