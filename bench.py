@@ -284,7 +284,7 @@ def kernel_name(w, cfg) -> str:
     return (f"spg::pipelined_gemm<{b(w.in_dtype == 'bf16')}, {b(w.b_layout == 'nk')}, "
             f"{cfg.block_m}, {cfg.block_n}, {cfg.block_k}, {cfg.wave_m}, {cfg.wave_n}, "
             f"{cfg.stages}, {b(cfg.swizzle)}, {cfg.staging}, {cfg.lookahead}, {cfg.schedule}, "
-            f"{b(pers)}>")
+            f"{b(pers)}, {cfg.mfma or 32}>")
 
 
 def measured_traffic(workload: str, cfg, w):
@@ -308,7 +308,7 @@ def measured_traffic(workload: str, cfg, w):
 
 
 def parse_tile(spec):
-    """'256x256x64:2[:swizzle[:group_m[:staging[:WMxWN[:lookahead[:schedule[:persistent[:store[:xcd_remap]]]]]]]]]'
+    """'256x256x64:2[:swizzle[:group_m[:staging[:WMxWN[:lookahead[:schedule[:persistent[:store[:xcd_remap[:mfma]]]]]]]]]]'
     -> the matching
     compiled configuration (the first one in the table when the wave tile is not given)."""
     import software_pipelined_tiled_gemm_amd as spg
@@ -327,11 +327,12 @@ def parse_tile(spec):
     pers = int(parts[8]) if len(parts) > 8 else 0
     store = int(parts[9]) if len(parts) > 9 else 0
     xcd = int(parts[10]) if len(parts) > 10 else 1
+    mfma = int(parts[11]) if len(parts) > 11 else 32
     for i in range(spg.gemm_num_configs()):
         c = spg.gemm_list_config(i)
         if wave is not None and (c.wave_m, c.wave_n) != wave:
             continue
-        if c.lookahead != look or c.schedule != sched or c.persistent != pers:
+        if c.lookahead != look or c.schedule != sched or c.persistent != pers or c.mfma != mfma:
             continue
         if (c.block_m, c.block_n, c.block_k, c.stages, c.swizzle, c.staging) == (bm, bn, bk, st, swz, stg):
             if gm:
@@ -346,8 +347,9 @@ def parse_tile(spec):
 # distinct kernel instantiation, so a profiler run over `--ablations` attributes
 # counters to the rows by kernel name.
 ABLATIONS = [
-    ("default: 256x256x64, S=2, 8 waves of 128x64, direct copies, A one slot deeper", "256x256x64:2:1:8:4:128x64:1:0"),
-    ("A and B rings both two deep (staging 0)", "256x256x64:2:1:8:0:128x64:1:0"),
+    ("default: 256x256x64, S=2, 8 waves of 128x64, direct copies, 16x16x32 MFMAs", "256x256x64:2:1:8:0:128x64:1:0:0:0:1:16"),
+    ("32x32x16 MFMAs (same tile)", "256x256x64:2:1:8:0:128x64:1:0"),
+    ("32x32x16, A one slot deeper than B (staging 4)", "256x256x64:2:1:8:4:128x64:1:0"),
     ("no overlap (S=1, the serial loop), 4 waves", "256x256x64:1:1:8:0:128x128:1:0"),
     ("4 waves of 128x128 (one per SIMD), lookahead 1", "256x256x64:2:1:8:0:128x128:1:0"),
     ("4 waves of 128x128, lookahead 2", "256x256x64:2:1:8:0:128x128:2:0"),
@@ -394,7 +396,7 @@ def main():
     ap.add_argument("--workload", default="nn_bf16_8192",
                     help="workload name from workloads.WORKLOADS")
     ap.add_argument("--tile", default=None,
-                    help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging[:WMxWN[:lookahead[:schedule[:persistent[:store[:xcd_remap]]]]]]]]] "
+                    help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging[:WMxWN[:lookahead[:schedule[:persistent[:store[:xcd_remap[:mfma]]]]]]]]]] "
                          "(default: the library's choice)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra lines (fp16 8192^3, the 8-GPU shard, the standalone "

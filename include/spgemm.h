@@ -112,6 +112,9 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1, GEMM_EPI_RELU = 2 } ge
  *                       from registers (4 consecutive outputs per store; the ablation
  *                       of the staging).  fp32 output and the persistent and
  *                       wave-specialized modes always stage.
+ *   mfma                32 (or 0) = v_mfma_f32_32x32x16 tiles; 16 = v_mfma_f32_16x16x32
+ *                       tiles (block_k 64, lookahead 1, not persistent): the same
+ *                       flops with half the accumulator register traffic per flop
  * The LDS a configuration needs is stages * (block_m + block_n) * block_k * 2 bytes
  * (the shared-memory bound of the TileLang tutorial's shared_bytes()), plus
  * block_m * block_k * 2 for staging 4, at most 160 KiB. */
@@ -127,6 +130,7 @@ typedef struct {
     int32_t schedule;
     int32_t persistent;
     int32_t store;
+    int32_t mfma;
 } gemm_tile_config;
 
 typedef struct gemm_plan* gemm_handle;

@@ -42,7 +42,8 @@ class TileConfig(ctypes.Structure):
                 ("swizzle", ctypes.c_int32), ("group_m", ctypes.c_int32),
                 ("xcd_remap", ctypes.c_int32), ("staging", ctypes.c_int32),
                 ("lookahead", ctypes.c_int32), ("schedule", ctypes.c_int32),
-                ("persistent", ctypes.c_int32), ("store", ctypes.c_int32)]
+                ("persistent", ctypes.c_int32), ("store", ctypes.c_int32),
+                ("mfma", ctypes.c_int32)]
 
     def __init__(self, **kw):
         kw.setdefault("lookahead", 1)
@@ -65,7 +66,8 @@ class TileConfig(ctypes.Structure):
                 f"group_m={d['group_m']}, xcd_remap={d['xcd_remap']}, "
                 f"staging={STAGING.get(d['staging'], d['staging'])}, lookahead={d['lookahead']}, "
                 f"schedule={'compiler' if d['schedule'] else 'manual'}"
-                f"{', persistent' if d['persistent'] else ''}{', direct store' if d['store'] else ''})")
+                f"{', persistent' if d['persistent'] else ''}{', direct store' if d['store'] else ''}"
+                f"{', mfma 16x16x32' if d['mfma'] == 16 else ''})")
 
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_get_config", "gemm_autotune",

@@ -134,21 +134,28 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Swizzle of K-contiguous tiles (A, and B stored [N,K]) with BK = 64: a row holds
-// 64 halves = 8 chunks of 16 B; logical chunk c of row r lives at chunk c ^ kswz(r).
-// Rows r..r+7 get distinct XOR values and rows r, r+8 differ in the low bit,
-// so 8 consecutive lanes (one 128-B bank sweep) or 16 (one 256-B sweep) reading
-// the same logical chunk of consecutive rows never share a bank.
+// 64 halves = 8 chunks of 16 B; logical chunk c of row r lives at chunk c ^ kswz(r),
+// kswz(r) = (r >> 1) & 7.  Rows 2j and 2j+1 (128 B apart) already fall on different
+// banks, so only pairs of rows need distinct XOR values.  Chosen by measurement
+// (SQ_LDS_BANK_CONFLICT over all 4096 XOR maps of the row's low 4 bits): 0% conflicts
+// for both fragment reads, 32 rows x 2 chunks (32x32x16) and 16 rows x 4 chunks
+// (16x16x32); the earlier (r & 7) ^ ((r >> 3) & 1) gave 0% and 25%.
 // With BK = 32 a row is 4 chunks (64 B) and the XOR is ((r>>1) ^ (r>>2)) & 3:
 // among 8 aligned rows, the 4 of equal parity (sharing a 128-B sweep) get
 // distinct values, and among 16 aligned rows the 4 of equal r%4 (sharing a
 // 256-B sweep) do too.
-__device__ __forceinline__ int kswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
 
 // Swizzle of N-contiguous B tiles ([K,N] storage): the 16-B chunk index of row
-// k is XOR-ed with {0, 6, 12, 10}[k & 3].  A transposing read covers 4
-// consecutive rows; this table gives those 4 rows distinct 32-B windows within
-// 128 B and distinct 64-B windows within 256 B.
-__device__ __forceinline__ int nswz(int k) { return (0xAC60 >> ((k & 3) * 4)) & 15; }
+// k is XOR-ed with {0, 6, 12, 10}[k & 3] ^ 2*(bit 3 of k).  A transposing read covers
+// 4 consecutive rows; the table gives those 4 rows distinct 32-B windows within
+// 128 B and distinct 64-B windows within 256 B, so one 16-lane group uses half of
+// the banks.  The second term moves rows k+8 .. k+11 onto the other half: with
+// 16x16x32 MFMAs the two 16-lane groups read together are rows k and k+8 of the
+// same columns (with 32x32x16 they are the same rows, 16 columns apart, which the
+// table alone separates).  Offsets of 4, 16 and 32 rows keep bit 3, so a lane's
+// swizzle is fixed over the k-steps of a k-tile.
+__device__ __forceinline__ int nswz(int k) { return ((0xAC60 >> ((k & 3) * 4)) & 15) ^ ((k >> 2) & 2); }
 
 __device__ __forceinline__ float gelu_tanh(float x) {
     // 0.5 x (1 + tanh(u)) == x * sigmoid(2u) == x / (1 + exp(-2u)),
@@ -210,6 +217,20 @@ __device__ __forceinline__ void tile_of(int wg, const KArgs& a, int& tm, int& tn
     const int in = wg - g * gsz;
     tm = first + in % gm;
     tn = in / gm;
+}
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x32_{f16,bf16}: x supplies rows 0..15 (lane l: row l%16, k 8(l/16)..+7),
+// y columns 0..15 likewise; lane l receives D[4(l/16) + 0..3][l%16]
+template <bool BF16>
+__device__ __forceinline__ floatx4 mfma16(const u32x4& x, const u32x4& y, const floatx4& c) {
+    if constexpr (BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
+                                                       __builtin_bit_cast(bf16x8, y), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, x),
+                                                      __builtin_bit_cast(halfx8, y), c, 0, 0, 0);
 }
 
 template <bool BF16>
@@ -313,13 +334,91 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TN][TM], char* 
     }
 }
 
+// The staged epilogue for 16x16x32 accumulators: lane l holds C[bm*16 + l%16][bn*16 +
+// 4(l/16) + 0..3]; a staged 32-row block is the accumulators of bm = 2g and 2g+1.  The
+// staging layout and the read-back are those of store_tile.
+template <int OD, int EPI, int TM, int TN, int WN, int NP = 1>
+__device__ __forceinline__ void store_tile16(const floatx4 (&acc)[TN][TM], char* stg,
+                                             const KArgs& args, int m_base, int n_base, int lane) {
+    constexpr int OB = OD == kOutF32 ? 4 : 2;
+    constexpr int ROWB = WN * OB;
+    constexpr int CPR = ROWB / 16;
+    constexpr int E16 = 16 / OB;
+    constexpr int PASSB = 32 * ROWB;
+    constexpr int NB32 = TM / 2;                      // 32-row blocks
+    static_assert(CPR == 8 || CPR == 16 || CPR == 32, "staging swizzle assumes 8..32 chunks");
+    static_assert(TM % 2 == 0 && NB32 % NP == 0, "blocks per round must divide the wave's blocks");
+    auto swz = [](int row) { return CPR >= 16 ? (row & 15) : ((row >> 1) & 7); };
+    const int M = args.M, N = args.N;
+    const bool vec_ok = (N % E16) == 0;
+    const int lrow = lane & 15;
+#pragma unroll
+    for (int g = 0; g < NB32; g += NP) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            char* sp = stg + p * PASSB;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int bm = 2 * (g + p) + h;
+                const int row = h * 16 + lrow;
+#pragma unroll
+                for (int bn = 0; bn < TN; ++bn) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = epi_t<EPI>(acc[bn][bm][e]);
+                    const int byte = (bn * 16 + 4 * (lane >> 4)) * OB;
+                    char* dst = sp + row * ROWB + (((byte >> 4) ^ swz(row)) << 4) + (byte & 15);
+                    if constexpr (OD == kOutF32) {
+                        *(SPG_LDS u32x4*)dst = u32x4{__builtin_bit_cast(uint32_t, v[0]),
+                                                     __builtin_bit_cast(uint32_t, v[1]),
+                                                     __builtin_bit_cast(uint32_t, v[2]),
+                                                     __builtin_bit_cast(uint32_t, v[3])};
+                    } else {
+                        constexpr bool BF = OD == kOutBF16;
+                        const uint32_t p0 = (uint32_t)f32_to_bits(v[0], BF) | ((uint32_t)f32_to_bits(v[1], BF) << 16);
+                        const uint32_t p1 = (uint32_t)f32_to_bits(v[2], BF) | ((uint32_t)f32_to_bits(v[3], BF) << 16);
+                        *(SPG_LDS u32x2*)dst = u32x2{p0, p1};
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const char* sp = stg + p * PASSB;
+#pragma unroll 1
+            for (int it = 0; it < (32 * CPR) / 64; ++it) {
+                const int idx = it * 64 + lane;
+                const int row = idx / CPR;
+                const int ch = idx % CPR;
+                const u32x4 val = *(const SPG_LDS u32x4*)(sp + row * ROWB + ((ch ^ swz(row)) << 4));
+                const int gm = m_base + (g + p) * 32 + row;
+                const int gn = n_base + ch * E16;
+                if (gm < M && gn < N) {
+                    char* dstg = (char*)args.C + ((size_t)gm * N + gn) * OB;
+                    if (vec_ok && gn + E16 <= N) {
+                        *(u32x4*)dstg = val;
+                    } else {
+                        const int lim = (N - gn) < E16 ? (N - gn) : E16;
+                        for (int e = 0; e < lim; ++e) {
+                            if constexpr (OB == 4) ((uint32_t*)dstg)[e] = val[e];
+                            else ((uint16_t*)dstg)[e] = (uint16_t)(val[e >> 1] >> ((e & 1) * 16));
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
 // Epilogue without LDS staging (the ablation of the staged one), 16-bit outputs: each
 // lane stores its own accumulator values, 4 consecutive outputs of one row per store,
 // so one wave instruction writes 32 rows x 2 segments of 8 bytes.  The epilogue and the
 // output type are applied per value at run time: one instantiation per kernel.
-template <int TM, int TN>
-__device__ __forceinline__ void store_direct16(const floatx16 (&acc)[TN][TM], const KArgs& args,
+template <int TM, int TN, int MI, typename AccV>
+__device__ __forceinline__ void store_direct16(const AccV (&acc)[TN][TM], const KArgs& args,
                                                int m_base, int n_base, int lane) {
+    constexpr int QN = MI == 32 ? 4 : 1;   // 4-output segments per accumulator tile and lane
     const int M = args.M, N = args.N;
     const int ep = args.epilogue;
     const bool bf = args.out_dtype == kOutBF16;
@@ -327,18 +426,19 @@ __device__ __forceinline__ void store_direct16(const floatx16 (&acc)[TN][TM], co
 #pragma unroll
     for (int bm = 0; bm < TM; ++bm) {
         __builtin_amdgcn_sched_barrier(0);
-        const int gm = m_base + bm * 32 + (lane & 31);
+        const int gm = m_base + bm * MI + (lane & (MI - 1));
 #pragma unroll
         for (int bn = 0; bn < TN; ++bn) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < QN; ++q) {
                 uint32_t h[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float x = epi_apply(acc[bn][bm][4 * q + e], ep);
                     h[e] = bf ? (uint32_t)f32_to_bits(x, true) : (uint32_t)f32_to_bits(x, false);
                 }
-                const int gn = n_base + bn * 32 + 8 * q + 4 * (lane >> 5);
+                const int gn = MI == 32 ? n_base + bn * 32 + 8 * q + 4 * (lane >> 5)
+                                        : n_base + bn * 16 + 4 * (lane >> 4);
                 if (gm < M && gn < N) {
                     uint16_t* dst = (uint16_t*)args.C + ((size_t)gm * N + gn);
                     if (vec_ok && gn + 4 <= N) {
@@ -374,13 +474,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_b(const void* base, 
                                              0x00020000);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int S>
+template <int BM, int BN, int BK, int WM, int WN, int S, int MI = 32>
 struct Geom {
     static constexpr int WAVES_N = BN / WN;
     static constexpr int NW = (BM / WM) * WAVES_N;
     static constexpr int NT = NW * 64;
-    static constexpr int TM = WM / 32, TN = WN / 32;
-    static constexpr int KSTEPS = BK / 16;             // MFMA k-steps per k-tile
+    // MFMA tiles per wave: MI x MI outputs each (32x32x16 or 16x16x32)
+    static constexpr int TM = WM / MI, TN = WN / MI;
+    static constexpr int KPS = MI == 32 ? 16 : 32;     // k of one MFMA step
+    static constexpr int KSTEPS = BK / KPS;            // MFMA k-steps per k-tile
+    static_assert(MI == 32 || MI == 16, "MFMA shape");
     static constexpr int ROWB = BK * 2;                // bytes of a K-contiguous tile row
     static constexpr int A_BYTES = BM * BK * 2;
     static constexpr int B_BYTES = BN * BK * 2;
@@ -451,11 +554,17 @@ __device__ __forceinline__ int kswz_t(int r) {
 // stays busy with the next tile's copies) and no workgroup-wide barrier is added.
 // The launcher uses it only when K % BK == 0 (no partial k-tile), the output is
 // 16-bit and, for B stored [K,N], N % BN == 0 (no column masks on the copies).
+//
+// MI selects the MFMA: 32 = v_mfma_f32_32x32x16 (16 accumulators per lane and tile, k 16
+// per step), 16 = v_mfma_f32_16x16x32 (4 accumulators per lane and tile, k 32 per step).
+// The LDS layout, the copies and the ring are the same; the fragment reads, the MFMA
+// call and the epilogue's accumulator layout differ.
 template <bool BF16, bool B_NK, int BM, int BN, int BK, int WM, int WN, int S, bool SWZ, int LDM,
-          int PF, int SCHED, bool PERS>
-__global__ void __launch_bounds__((Geom<BM, BN, BK, WM, WN, S>::NT))
+          int PF, int SCHED, bool PERS, int MI>
+__global__ void __launch_bounds__((Geom<BM, BN, BK, WM, WN, S, MI>::NT))
 pipelined_gemm(KArgs args) {
-    using G = Geom<BM, BN, BK, WM, WN, S>;
+    using G = Geom<BM, BN, BK, WM, WN, S, MI>;
+    static_assert(MI == 32 || (!PERS && PF == 1 && BK == 64), "16x16x32: BK 64, lookahead 1, one workgroup per tile");
     static_assert(LDM != 2 || S >= 3, "spread copies need a slot of slack");
     static_assert(PF == 1 || (PF == 2 && BK == 64 && S > 1), "lookahead 2 needs four k-steps per k-tile");
     static_assert(!PERS || (LDM == 0 && S >= 2), "persistent: direct copies and a ring of >= 2 slots");
@@ -705,11 +814,13 @@ pipelined_gemm(KArgs args) {
     // A (second MFMA operand): lane l reads row wm*WM + bm*32 + l%32,
     // k = kk*16 + (l/32)*8 .. +7  (16-B chunk 2kk + l/32).  The swizzle depends on
     // the row's low 4 bits only, which are those of l%32.
+    // (16x16x32: lane l reads row l%16, k = kk*32 + (l/16)*8 .. +7, chunk 4kk + l/16; the
+    // swizzle depends on the row's low 4 bits, the same for every 16-row fragment)
     int aoff[KSTEPS];
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
-        const int c = kk * 2 + (lane >> 5);
-        const int r = lane & 31;
+        const int c = MI == 32 ? kk * 2 + (lane >> 5) : kk * 4 + (lane >> 4);
+        const int r = lane & (MI - 1);
         aoff[kk] = (wm * WM + r) * ROWB + (SWZ ? (c ^ kswz_t<BK>(r)) : c) * 16;
     }
     // B (first MFMA operand): lane l needs column n = wn*WN + bn*32 + l%32 with the
@@ -718,30 +829,38 @@ pipelined_gemm(KArgs args) {
     if constexpr (B_NK) {
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-            const int c = kk * 2 + (lane >> 5);
-            const int r = lane & 31;
+            const int c = MI == 32 ? kk * 2 + (lane >> 5) : kk * 4 + (lane >> 4);
+            const int r = lane & (MI - 1);
             boff[kk] = (wn * WN + r) * ROWB + (SWZ ? (c ^ kswz_t<BK>(r)) : c) * 16;
         }
     } else {
         // ds_read_b64_tr_b16: in each 16-lane group, lane i supplies 8 B of row
         // (k0 + i/4) at columns (n0 + 4*(i%4)) .. +3 and receives column n0 + i of
-        // rows k0..k0+3.  Lanes 16-31 take columns +16, lanes 32-63 rows +8.
+        // rows k0..k0+3.  32x32x16: lanes 16-31 take columns +16, lanes 32-63 rows +8;
+        // 16x16x32: each 16-lane group takes rows +8 (k 8(l/16) .. +7 of the step).
         constexpr int RB = BN * 2;
-        const int kl = (lane >> 5) * 8 + ((lane & 15) >> 2);
+        const int kl = MI == 32 ? (lane >> 5) * 8 + ((lane & 15) >> 2) : (lane >> 4) * 8 + ((lane & 15) >> 2);
 #pragma unroll
         for (int bn = 0; bn < TN; ++bn) {
-            const int chunk = (wn * WN + bn * 32) / 8 + ((lane >> 4) & 1) * 2 + ((lane >> 1) & 1);
+            const int chunk = MI == 32 ? (wn * WN + bn * 32) / 8 + ((lane >> 4) & 1) * 2 + ((lane >> 1) & 1)
+                                       : (wn * WN + bn * 16) / 8 + ((lane >> 1) & 1);
             boff[bn] = kl * RB + (SWZ ? (chunk ^ nswz(kl)) : chunk) * 16 + (lane & 1) * 8;
         }
     }
 
-    floatx16 acc[TN][TM];
+    using AccV = std::conditional_t<MI == 32, floatx16, floatx4>;
+    constexpr int NACC = MI == 32 ? 16 : 4;   // accumulators per lane and MFMA tile
+    AccV acc[TN][TM];
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
         for (int j = 0; j < TM; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+            for (int e = 0; e < NACC; ++e) acc[i][j][e] = 0.0f;
+    auto mfma_step = [&](const u32x4& b, const u32x4& a, AccV& c) __attribute__((always_inline)) {
+        if constexpr (MI == 32) c = mfma<BF16>(b, a, c);
+        else c = mfma16<BF16>(b, a, c);
+    };
 
     // ---- persistent: the compute side of the k-tile stream ----------------------
     // (c_tile, c_kt): the tile and k-tile the MFMAs are on.  A tile's epilogue stages
@@ -778,15 +897,15 @@ pipelined_gemm(KArgs args) {
     auto read_op = [&](const Slot& slot, int kk, Frags& f, auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
         if constexpr (r < TM) {
-            f.a[r] = *(const SPG_LDS u32x4*)(slot.a + aoff[kk] + r * 32 * ROWB);
+            f.a[r] = *(const SPG_LDS u32x4*)(slot.a + aoff[kk] + r * MI * ROWB);
         } else if constexpr (B_NK) {
             constexpr int bn = r - TM;
-            f.b[bn] = *(const SPG_LDS u32x4*)(slot.b + boff[kk] + bn * 32 * ROWB);
+            f.b[bn] = *(const SPG_LDS u32x4*)(slot.b + boff[kk] + bn * MI * ROWB);
         } else {
             constexpr int bn = (r - TM) / 2, h = (r - TM) % 2;
             constexpr int RB = BN * 2;
             const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (SPG_LDS shortx4*)(slot.b + boff[bn] + (kk * 16 + h * 4) * RB));
+                (SPG_LDS shortx4*)(slot.b + boff[bn] + (kk * G::KPS + h * 4) * RB));
             const u32x2 v2 = __builtin_bit_cast(u32x2, v);
             f.b[bn][2 * h] = v2[0];
             f.b[bn][2 * h + 1] = v2[1];
@@ -800,7 +919,7 @@ pipelined_gemm(KArgs args) {
         for (int bn = 0; bn < TN; ++bn)
 #pragma unroll
             for (int bm = 0; bm < TM; ++bm)
-                acc[bn][bm] = mfma<BF16>(f.b[bn], f.a[bm], acc[bn][bm]);
+                mfma_step(f.b[bn], f.a[bm], acc[bn][bm]);
     };
     // keep each stage's loads and MFMAs together: no motion across stage boundaries
     auto fence = []() __attribute__((always_inline)) {
@@ -838,7 +957,7 @@ pipelined_gemm(KArgs args) {
             constexpr int i = decltype(ic)::value;
             if constexpr (i < NMMA) {
                 constexpr int bn = i / TM, bm = i % TM;
-                acc[bn][bm] = mfma<BF16>(now.b[bn], now.a[bm], acc[bn][bm]);
+                mfma_step(now.b[bn], now.a[bm], acc[bn][bm]);
             }
             if constexpr (MD == 1 && i < NCP) {
                 // the A-deep ring issues B before A (see LDM 4)
@@ -1058,7 +1177,7 @@ pipelined_gemm(KArgs args) {
 #pragma unroll
                         for (int j = 0; j < TM; ++j)
 #pragma unroll
-                            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+                            for (int e = 0; e < NACC; ++e) acc[i][j][e] = 0.0f;
                 }
             }
         };
@@ -1098,7 +1217,7 @@ pipelined_gemm(KArgs args) {
         // before the ring is reused for staging
         wait_vmcnt<0>();
         if (args.store_direct && args.out_dtype != kOutF32) {
-            store_direct16<TM, TN>(acc, args, m0 + wm * WM, n0 + wn * WN, lane);
+            store_direct16<TM, TN, MI>(acc, args, m0 + wm * WM, n0 + wn * WN, lane);
             return;
         }
         __syncthreads();  // the ring is drained and free for staging
@@ -1117,10 +1236,17 @@ pipelined_gemm(KArgs args) {
             constexpr int OD = decltype(odc)::value;
             // several blocks per round only for one wave per SIMD: with two, the partner
             // wave already covers the latency (measured: +1.2% with 4 waves, -0.4% with 8)
-            constexpr int NP = G::NW > 4 ? 1 : blocks_per_round<TM, WN, OD == kOutF32 ? 4 : 2>(G::STGW);
-            if (ep == kEpiGelu) store_tile<OD, kEpiGelu, TM, TN, WN, NP>(acc, stg, args, m_base, n_base, lane);
-            else if (ep == kEpiRelu) store_tile<OD, kEpiRelu, TM, TN, WN, NP>(acc, stg, args, m_base, n_base, lane);
-            else store_tile<OD, kEpiNone, TM, TN, WN, NP>(acc, stg, args, m_base, n_base, lane);
+            constexpr int NB32 = TM * MI / 32;   // 32-row blocks of the wave tile
+            constexpr int NP = G::NW > 4 ? 1 : blocks_per_round<NB32, WN, OD == kOutF32 ? 4 : 2>(G::STGW);
+            if constexpr (MI == 32) {
+                if (ep == kEpiGelu) store_tile<OD, kEpiGelu, TM, TN, WN, NP>(acc, stg, args, m_base, n_base, lane);
+                else if (ep == kEpiRelu) store_tile<OD, kEpiRelu, TM, TN, WN, NP>(acc, stg, args, m_base, n_base, lane);
+                else store_tile<OD, kEpiNone, TM, TN, WN, NP>(acc, stg, args, m_base, n_base, lane);
+            } else {
+                if (ep == kEpiGelu) store_tile16<OD, kEpiGelu, TM, TN, WN, NP>(acc, stg, args, m_base, n_base, lane);
+                else if (ep == kEpiRelu) store_tile16<OD, kEpiRelu, TM, TN, WN, NP>(acc, stg, args, m_base, n_base, lane);
+                else store_tile16<OD, kEpiNone, TM, TN, WN, NP>(acc, stg, args, m_base, n_base, lane);
+            }
         };
         if (od == kOutF32) store_as(std::integral_constant<int, kOutF32>{});
         else if (od == kOutBF16) store_as(std::integral_constant<int, kOutBF16>{});

@@ -198,8 +198,8 @@ def test_heuristic_tiles(L):
         return c
     big = cfg(8192, 8192, 8192)
     assert (big.block_m, big.block_n, big.wave_m, big.wave_n) == (256, 256, 128, 64)
-    assert big.staging == 4                 # A-deep ring on grids of two or more rounds
-    assert cfg(4096, 4096, 4096).staging == 0
+    assert (big.mfma, big.staging) == (16, 0)     # 16x16x32 MFMAs on the 8-wave tiles
+    assert cfg(1024, 8192, 8192).mfma == 16 and cfg(256, 256, 256).mfma == 32
     small = cfg(256, 256, 256)
     assert (small.block_m, small.block_n) == (128, 128)
     # the cost model: rounds of 256 CUs x tile area / per-tile throughput

@@ -42,24 +42,26 @@ def test_all_variants_ragged(in_dtype, b_layout):
         C, used = G.run(w, a, b, force=cfg)
         got = G.c_values(C, w)
         G.check(w, a, b, got)
-        results[repr(cfg)] = got
-    # every pipelined configuration keeps the same per-element k order (k-tiles in
-    # ascending order, 16-wide MFMA steps in ascending order), so the results must
-    # be bitwise identical: a slot reused too early would break this
-    vals = list(results.values())
-    for v in vals[1:]:
-        assert np.array_equal(v, vals[0])
+        results.setdefault(cfg.mfma, []).append(got)
+    # every pipelined configuration with the same MFMA shape keeps the same per-element
+    # k order (k-tiles ascending, MFMA steps of 16 or 32 k ascending), so their results
+    # must be bitwise identical: a slot reused too early would break this
+    assert set(results) == {16, 32}
+    for vals in results.values():
+        for v in vals[1:]:
+            assert np.array_equal(v, vals[0])
 
 
 @pytest.mark.parametrize("out_dtype", [W.BF16, W.F32])
 def test_relu_every_wave_tile(out_dtype):
-    # the epilogue is instantiated per (output type, epilogue, wave tile): run ReLU on one
-    # configuration of every distinct block and wave tile, ragged in M, N and K
+    # the epilogue is instantiated per (output type, epilogue, wave tile, MFMA shape): run
+    # ReLU on one configuration of every distinct block, wave tile and MFMA shape, ragged
+    # in M, N and K
     w = W.custom(520, 648, 616, W.F16, out_dtype, W.B_KN, "relu", ("uniform", -1.0, 1.0))
     a, b = W.make_inputs(w)
     seen = set()
     for cfg in _variants():
-        key = (cfg.block_m, cfg.block_n, cfg.wave_m, cfg.wave_n)
+        key = (cfg.block_m, cfg.block_n, cfg.wave_m, cfg.wave_n, cfg.mfma)
         if key in seen:
             continue
         seen.add(key)
@@ -142,6 +144,25 @@ def test_misaligned_pointers_take_the_simple_path():
     G.check(w, a, b, G.c_values(C, w))
 
 
+@pytest.mark.parametrize("out_dtype", [W.BF16, W.F32])
+def test_mfma16_gelu_and_direct_store(out_dtype):
+    # the 16x16x32 accumulator layout through the staged epilogue with GELU (all output
+    # types) and through the direct store, against the oracle, ragged in M, N and K
+    m16 = [c for c in _variants() if c.mfma == 16 and c.staging == 0]
+    assert m16
+    for c in m16:
+        for layout in (W.B_KN, W.B_NK):
+            w = W.custom(300, 520, 200, W.BF16, out_dtype, layout, "gelu_tanh", ("uniform", -1.0, 1.0))
+            a, b = W.make_inputs(w)
+            _log(f"mfma16 {c} {w.describe()}")
+            C, _ = G.run(w, a, b, force=c)
+            got = G.c_values(C, w)
+            G.check(w, a, b, got)
+            d = spg.TileConfig.from_dict(dict(c.as_dict(), store=1))
+            C2, _ = G.run(w, a, b, force=d)
+            assert np.array_equal(G.c_values(C2, w), got)
+
+
 def test_misaligned_output_takes_the_simple_path():
     import torch
     w = W.custom(100, 72, 64, W.BF16, W.BF16, W.B_KN)
@@ -161,7 +182,7 @@ def test_direct_store_epilogue(out_dtype):
     # the epilogue stored from registers (the ablation of LDS staging): same values as the
     # staged one, masked edges, N % 4 != 0 element stores; fp32 output keeps the staging
     picks = [c for c in _variants() if c.staging == 0 and c.persistent == 0 and c.schedule == 0
-             and c.lookahead == 1 and c.swizzle == 1 and c.stages >= 2
+             and c.lookahead == 1 and c.swizzle == 1 and c.stages >= 2 and c.mfma == 32
              and (c.block_m, c.block_n, c.wave_m, c.wave_n) in ((256, 256, 128, 64), (128, 128, 64, 64))]
     one_per_tile = {}
     for c in picks:
@@ -279,13 +300,13 @@ def test_a_deep_ring_every_tail():
     # the A-deep ring runs six k-tiles per iteration and then the rest one by one: every
     # remainder 0..5, fewer k-tiles than one iteration, a leading partial k-tile, both
     # layouts; bitwise equal to the two-deep ring (same k order) and within tolerance
-    deep = [c for c in _variants() if c.staging == 4]
+    deep = [c for c in _variants() if c.staging == 4 and c.mfma == 32]
     assert deep, "no A-deep configuration compiled"
     d = deep[0]
     twin = [c for c in _variants() if c.staging == 0 and (c.block_m, c.block_n, c.block_k, c.stages,
-            c.wave_m, c.wave_n, c.lookahead, c.schedule, c.persistent) ==
+            c.wave_m, c.wave_n, c.lookahead, c.schedule, c.persistent, c.mfma) ==
             (d.block_m, d.block_n, d.block_k, d.stages, d.wave_m, d.wave_n, d.lookahead, d.schedule,
-             d.persistent)][0]
+             d.persistent, d.mfma)][0]
     for K in (40, 64, 128, 192, 256, 320, 384, 448, 760, 1024):
         for layout in (W.B_KN, W.B_NK):
             w = W.custom(300, 520, K, W.BF16, W.BF16, layout, "none", ("uniform", -1.0, 1.0))
