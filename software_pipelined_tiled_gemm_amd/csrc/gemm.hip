@@ -159,14 +159,20 @@ gemm_tile_config heuristic(int64_t M, int64_t N) {
     // Estimated time of a candidate = rounds of the 256 CUs it needs x its tile's
     // area / its measured per-tile throughput relative to 256x256 (bf16 NN 8192^3
     // and the 1024x8192x8192 shard on MI355X: 256x128 runs at 0.91 of the 256x256
-    // rate per output, 128x128 at 0.66).  The smallest estimate wins: 256x256 as long
-    // as the grid is not much less than one round, 256x128 for half-size grids,
-    // 128x128 for small problems.
+    // rate per output, 128x128 at 0.66, 192x256 at 0.80 (3072x4096x4096) to 0.88
+    // (6144x8192x8192: 4 rounds of 192x256 against 3 of 256x256, 623 vs 549 us)).
+    // The smallest estimate wins: 256x256 as long as the grid is not much less than
+    // one round, 192x256 where its rows fill the CUs better (M = 3072: 16 x 16 tiles
+    // against 12 x 16), 256x128 for half-size grids, 128x128 for small problems.
+    // The 8-wave tiles run 16x16x32 MFMAs (measured against 32x32x16 with the same
+    // tile, interleaved in one process, +2..9% on every benchmark shape; fp16 and
+    // [N,K] B gain the most), the 4-wave 128x128 tile 32x32x16.
     const int64_t cus = 256;
-    struct Cand { int bm, bn, bk, st, wm, wn; double eff; };
-    const Cand cands[] = {{256, 256, 64, 2, 128, 64, 1.0},
-                          {256, 128, 64, 3, 64, 64, 0.91},
-                          {128, 128, 64, 3, 64, 64, 0.66}};
+    struct Cand { int bm, bn, bk, st, wm, wn, mfma; double eff; };
+    const Cand cands[] = {{256, 256, 64, 2, 128, 64, 16, 1.0},
+                          {192, 256, 64, 2, 96, 64, 16, 0.85},
+                          {256, 128, 64, 3, 64, 64, 16, 0.91},
+                          {128, 128, 64, 3, 64, 64, 32, 0.66}};
     const Cand* best = nullptr;
     double best_t = 0.0;
     for (const Cand& c : cands) {
@@ -174,11 +180,7 @@ gemm_tile_config heuristic(int64_t M, int64_t N) {
         const double t = (double)((tiles + cus - 1) / cus) * c.bm * c.bn / c.eff;
         if (!best || t < best_t) { best = &c; best_t = t; }
     }
-    // the 8-wave tiles run 16x16x32 MFMAs: measured against 32x32x16 with the same
-    // tile, interleaved in one process, +2..9% on every benchmark shape (fp16 and
-    // [N,K] B gain the most)
-    const int mfma = best->bm == 256 ? 16 : 32;
-    gemm_tile_config c = find_cfg(best->bm, best->bn, best->bk, best->st, 0, best->wm, best->wn, 0, mfma)->cfg;
+    gemm_tile_config c = find_cfg(best->bm, best->bn, best->bk, best->st, 0, best->wm, best->wn, 0, best->mfma)->cfg;
     // 8 tile rows per raster group on tall grids; 4 on grids of at most 16 tile rows
     c.group_m = (M + best->bm - 1) / best->bm > 16 ? 8 : 4;
     c.xcd_remap = 1;

@@ -205,8 +205,10 @@ def test_heuristic_tiles(L):
     # the cost model: rounds of 256 CUs x tile area / per-tile throughput
     shard = cfg(1024, 8192, 8192)           # 128 tiles of 256x256, 256 of 256x128
     assert (shard.block_m, shard.block_n) == (256, 128)
-    gelu = cfg(3072, 4096, 4096)            # 192 tiles of 256x256: one round
-    assert (gelu.block_m, gelu.block_n) == (256, 256)
+    gelu = cfg(3072, 4096, 4096)            # 192 tiles of 256x256, 256 of 192x256: one round
+    assert (gelu.block_m, gelu.block_n, gelu.wave_m, gelu.mfma) == (192, 256, 96, 16)
+    tall = cfg(6144, 8192, 8192)            # 3 rounds of 256x256 against 4 of 192x256
+    assert (tall.block_m, tall.block_n) == (256, 256)
     ragged = cfg(3000, 5000, 1000)          # 12 x 20 = 240 tiles of 256x256
     assert (ragged.block_m, ragged.block_n) == (256, 256)
     assert cfg(4096, 4096, 4096).group_m == 4 and big.group_m == 8
