@@ -372,10 +372,27 @@ ABLATIONS = [
     ("256x128 tile, 8 waves of 64x64, S=3, release delay 1", "256x128x64:3:1:8:5:64x64:1:0"),
 ]
 
+# The tile-shape choice at the fused-GELU workload (3072x4096x4096, bf16 NN): how many
+# tiles each shape makes against the 256 CUs.
+GELU_ABLATIONS = [
+    ("default: 192x256x64, S=2, 8 waves of 96x64, 16x16x32 (256 tiles: one per CU)", "192x256x64:2:1:4:0:96x64:1:0:0:0:1:16"),
+    ("256x256x64, S=2, 8 waves of 128x64, 16x16x32 (192 tiles: 64 CUs idle)", "256x256x64:2:1:4:0:128x64:1:0:0:0:1:16"),
+    ("256x256x64, 32x32x16 (192 tiles)", "256x256x64:2:1:4:0:128x64:1:0"),
+    ("256x128x64, S=3, 8 waves of 64x64, 16x16x32 (384 tiles: 1.5 rounds)", "256x128x64:3:1:4:0:64x64:1:0:0:0:1:16"),
+    ("128x128x64, S=3, 4 waves of 64x64, 32x32x16 (768 tiles: 3 rounds)", "128x128x64:3:1:4:0:64x64:1:0"),
+]
+
+ABLATIONS_BY_WORKLOAD = {"nn_bf16_3072x4096x4096_gelu": GELU_ABLATIONS}
+
+
+def ablations_for(workload):
+    """The ablation rows of a workload (the design-choice list unless it has its own)."""
+    return ABLATIONS_BY_WORKLOAD.get(workload, ABLATIONS)
+
 
 def run_ablations(w, steps, warmup):
     rows = []
-    for label, spec in ABLATIONS:
+    for label, spec in ablations_for(w.name):
         cfg = parse_tile(spec)
         _, k, used = time_gemm(w, steps, warmup, cfg)
         rows.append({"label": label, "tile": spec, "kernel_us": round(k * 1e3, 2),
@@ -402,8 +419,9 @@ def main():
                     help="skip the extra lines (fp16 8192^3, the 8-GPU shard, the standalone "
                          "GELU, fused vs unfused GELU GEMM, the sustained clock)")
     ap.add_argument("--ablations", action="store_true",
-                    help="time the design-choice ablations (ABLATIONS) on the workload instead "
-                         "of the benchmark line")
+                    help="time the design-choice ablations on the workload instead of the "
+                         "benchmark line (ABLATIONS, or the workload's own list in "
+                         "ABLATIONS_BY_WORKLOAD)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy 5 times, so that HBM "
                          "byte counters can be scaled against a kernel of known traffic")

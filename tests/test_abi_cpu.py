@@ -212,3 +212,14 @@ def test_heuristic_tiles(L):
     ragged = cfg(3000, 5000, 1000)          # 12 x 20 = 240 tiles of 256x256
     assert (ragged.block_m, ragged.block_n) == (256, 256)
     assert cfg(4096, 4096, 4096).group_m == 4 and big.group_m == 8
+
+
+def test_every_ablation_row_names_a_compiled_configuration(L):
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    for name in ["nn_bf16_8192", *bench.ABLATIONS_BY_WORKLOAD]:
+        specs = [s for _, s in bench.ablations_for(name)]
+        assert len(set(specs)) == len(specs), name
+        for spec in specs:
+            bench.parse_tile(spec)   # SystemExit if no compiled configuration matches
