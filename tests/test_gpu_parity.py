@@ -361,3 +361,21 @@ def test_workload_full_size(name):
     Cf = C.float() if w.out_dtype == W.F32 else (
         C.view(torch.bfloat16).float() if w.out_dtype == W.BF16 else C.view(torch.float16).float())
     assert bool(torch.isfinite(Cf).all())
+
+
+def test_full_size_fp32_output_isolates_the_accumulation():
+    """bf16 NN 8192^3 in the tile configuration the benchmark times, with an fp32 output:
+    nothing is rounded to 16 bits, so the literal bound (1e-4 for an fp32 output) applies
+    to the fp32 accumulation itself, on sampled rows against the oracle."""
+    w = W.custom(8192, 8192, 8192, W.BF16, W.F32, W.B_KN, "none", ("uniform", -1.0, 1.0),
+                 name="nn_bf16_8192_f32out")
+    _log(f"workload {w.name}: {w.describe()}")
+    a, b = W.make_inputs(w)
+    C, cfg = G.run(w, a, b)
+    _log(f"  config {cfg}")
+    assert (cfg.block_m, cfg.block_n, cfg.mfma) == (256, 256, 16)
+    r = np.random.Generator(np.random.PCG64(78))
+    rows = np.sort(np.concatenate([[0, w.M - 1], r.choice(w.M, 30, replace=False)]))
+    res = G.check(w, a, b, G.c_values(C, w, rows), rows=rows)
+    _log(f"  sampled rows: err_lit={res['err_lit']:.3e} err_q={res['err_q']:.3e}")
+    assert res["err_lit"] <= 1e-4
