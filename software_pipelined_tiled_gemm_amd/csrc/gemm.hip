@@ -181,8 +181,10 @@ gemm_tile_config heuristic(int64_t M, int64_t N) {
         if (!best || t < best_t) { best = &c; best_t = t; }
     }
     gemm_tile_config c = find_cfg(best->bm, best->bn, best->bk, best->st, 0, best->wm, best->wn, 0, best->mfma)->cfg;
-    // 8 tile rows per raster group on tall grids; 4 on grids of at most 16 tile rows
-    c.group_m = (M + best->bm - 1) / best->bm > 16 ? 8 : 4;
+    // 4 tile rows per raster group: with the 16x16x32 tiles at 8192^3 (32 tile rows),
+    // measured interleaved: group_m 2 / 4 / 8 / 16 / 32 = 758 / 730 / 740 / 752 / 911 us
+    // (NN) and 765 / 733 /741 / 766 / 934 us (TN); the 32x32x16 kernel preferred 8
+    c.group_m = kDefaultGroupM;
     c.xcd_remap = 1;
     return c;
 }

@@ -211,7 +211,7 @@ def test_heuristic_tiles(L):
     assert (tall.block_m, tall.block_n) == (256, 256)
     ragged = cfg(3000, 5000, 1000)          # 12 x 20 = 240 tiles of 256x256
     assert (ragged.block_m, ragged.block_n) == (256, 256)
-    assert cfg(4096, 4096, 4096).group_m == 4 and big.group_m == 8
+    assert cfg(4096, 4096, 4096).group_m == 4 and big.group_m == 4
 
 
 def test_every_ablation_row_names_a_compiled_configuration(L):
