@@ -147,9 +147,10 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
                         const gemm_tile_config* force);
 
 /* Enqueue C = epi(A . B) on `stream` (0 = null stream).  Asynchronous: no
- * allocation, no synchronization.  A, B, C are device pointers as described
- * above.  Errors: INVALID_ARG (NULL handle, or NULL pointer with a non-empty
- * operand), HIP (launch failure). */
+ * allocation, no synchronization, exactly one kernel launch, so it may be captured
+ * into a HIP graph (the pointers are baked into the captured launch).  A, B, C are
+ * device pointers as described above.  Errors: INVALID_ARG (NULL handle, or NULL
+ * pointer with a non-empty operand), HIP (launch failure). */
 gemm_status gemm_run(gemm_handle h, const void* A, const void* B, void* C, hipStream_t stream);
 
 /* Release a plan.  NULL is a no-op. */

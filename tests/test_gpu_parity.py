@@ -379,3 +379,41 @@ def test_full_size_fp32_output_isolates_the_accumulation():
     res = G.check(w, a, b, G.c_values(C, w, rows), rows=rows)
     _log(f"  sampled rows: err_lit={res['err_lit']:.3e} err_q={res['err_q']:.3e}")
     assert res["err_lit"] <= 1e-4
+
+
+@pytest.mark.parametrize("shape", [(1000, 1100, 700), (3072, 4096, 4096)], ids=["ragged", "gelu_workload"])
+def test_gemm_run_replays_in_a_hip_graph(shape):
+    """gemm_run neither allocates nor synchronizes, so a caller can capture it in a HIP
+    graph.  Captured once (torch.cuda.graph) and replayed several times, with eager work
+    and synchronizations between the replays, every replay gives the eager result bitwise
+    (and the eager result is within tolerance of the oracle on sampled rows)."""
+    import torch
+    M, N, K = shape
+    w = W.custom(M, N, K, W.BF16, W.BF16, W.B_KN, "gelu_tanh", ("uniform", -1.0, 1.0),
+                 name="graph_replay")
+    _log(f"graph replay: {w.describe()}")
+    a, b = W.make_inputs(w)
+    A, B = G.to_dev(a), G.to_dev(b)
+    C_eager, C_graph = G.alloc_c(w), G.alloc_c(w)
+    with spg.Gemm(M, N, K, w.in_dtype, w.out_dtype, w.b_layout, w.epilogue) as g:
+        _log(f"  config {g.config()}")
+        g(A, B, C_eager)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            g(A, B, C_graph)                 # warm-up launch on a side stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            g(A, B, C_graph)                 # gemm_run on the capture stream
+        for i in range(4):
+            C_graph.fill_(-1)                # eager work between the replays
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(C_graph, C_eager), f"replay {i}"
+        del graph
+    rows = np.array([0, M // 3, M - 1])
+    G.check(w, a, b, G.c_values(C_eager, w, rows), rows=rows)
