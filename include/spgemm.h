@@ -65,17 +65,21 @@ typedef enum {
 typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1, GEMM_EPI_RELU = 2 } gemm_epilogue;
 
 /* Tile configuration of the pipelined kernel.
- *   block_m x block_n   output tile of one workgroup (128 or 256 each)
+ *   block_m x block_n   output tile of one workgroup (128, 192 or 256 rows; 128 or
+ *                       256 columns; gemm_list_configs() lists the compiled ones)
  *   block_k             K extent of one pipeline stage (32 or 64)
  *   stages              LDS ring depth S (1 = no overlap, the serial K loop of the
  *                       TileLang tutorial's matmul_plain; 2..4 = loads of k-tile t+S-1
  *                       in flight while k-tile t is multiplied)
  *   wave_m x wave_n     output tile of one 64-lane wave (multiples of 32)
  *   swizzle             1 = XOR-swizzled LDS layout, 0 = plain row layout (ablation)
- *   group_m             tile-raster group height in tiles (L2 reuse); 0 = default
+ *   group_m             tile-raster group height in tiles (L2 reuse); 0 = default (4)
  *   xcd_remap           1 = give each of the 8 XCDs a contiguous range of tiles
  *   staging             0 = k-tiles are copied straight from memory into LDS
- *                       (buffer_load ... lds), a k-tile's copies issued together;
+ *                       (buffer_load ... lds), a k-tile's copies issued in the
+ *                       first stage after the barrier that frees their slot (one per
+ *                       MFMA step, or one every second step where the stage has at
+ *                       least twice as many MFMAs as copies);
  *                       1 = copied into VGPRs one k-tile ahead and written to LDS
  *                       with ds_write_b128; 2 = straight into LDS, the copies of a
  *                       k-tile spread evenly between two barriers (stages >= 3);
