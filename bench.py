@@ -349,6 +349,12 @@ def parse_tile(spec):
 ABLATIONS = [
     ("default: 256x256x64, S=2, 8 waves of 128x64, direct copies, 16x16x32 MFMAs, group_m 4", "256x256x64:2:1:4:0:128x64:1:0:0:0:1:16"),
     ("the same with group_m 8 (the 32x32x16 kernel's best)", "256x256x64:2:1:8:0:128x64:1:0:0:0:1:16"),
+    ("16x16x32, no swizzle", "256x256x64:2:0:4:0:128x64:1:0:0:0:1:16"),
+    ("16x16x32, no overlap (S=1, the serial loop)", "256x256x64:1:1:4:0:128x64:1:0:0:0:1:16"),
+    ("16x16x32, compiler-placed schedule", "256x256x64:2:1:4:0:128x64:1:1:0:0:1:16"),
+    ("16x16x32, epilogue stored from registers (no LDS staging)", "256x256x64:2:1:4:0:128x64:1:0:0:1:1:16"),
+    ("16x16x32, no tile remap (row-major raster, no XCD ranges)", "256x256x64:2:1:1:0:128x64:1:0:0:0:0:16"),
+    ("16x16x32, 256x128 tile, 8 waves of 64x64, S=3", "256x128x64:3:1:4:0:64x64:1:0:0:0:1:16"),
     ("32x32x16 MFMAs (same tile)", "256x256x64:2:1:8:0:128x64:1:0"),
     ("32x32x16, A one slot deeper than B (staging 4)", "256x256x64:2:1:8:4:128x64:1:0"),
     ("no overlap (S=1, the serial loop), 4 waves", "256x256x64:1:1:8:0:128x128:1:0"),
