@@ -1148,8 +1148,10 @@ pipelined_gemm(KArgs args) {
             lds_barrier();
             // The stages after the barrier run at raised wave priority: with two waves
             // per SIMD the one that passed the barrier first keeps the matrix pipe
-            // while its partner is still in the barrier's wake (measured +1.7% at
-            // 8192^3 with 128x64 wave tiles).
+            // while its partner is still in the barrier's wake (measured at 8192^3 with
+            // 128x64 wave tiles: +1.7% with 32x32x16; +1.2% NN and +2.6% TN with
+            // 16x16x32, where no raised priority, dropping it part-way through the stage
+            // or raising it before the barrier instead were all slower).
             __builtin_amdgcn_s_setprio(1);
             {
                 // the window that starts here: k-tile t+S into cur
