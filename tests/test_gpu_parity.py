@@ -363,12 +363,14 @@ def test_workload_full_size(name):
     assert bool(torch.isfinite(Cf).all())
 
 
-def test_full_size_fp32_output_isolates_the_accumulation():
-    """bf16 NN 8192^3 in the tile configuration the benchmark times, with an fp32 output:
-    nothing is rounded to 16 bits, so the literal bound (1e-4 for an fp32 output) applies
-    to the fp32 accumulation itself, on sampled rows against the oracle."""
-    w = W.custom(8192, 8192, 8192, W.BF16, W.F32, W.B_KN, "none", ("uniform", -1.0, 1.0),
-                 name="nn_bf16_8192_f32out")
+@pytest.mark.parametrize("b_layout", [W.B_KN, W.B_NK])
+def test_full_size_fp32_output_isolates_the_accumulation(b_layout):
+    """bf16 8192^3 (B stored [K,N] or [N,K]) in the tile configuration the benchmark times,
+    with an fp32 output: nothing is rounded to 16 bits, so the literal bound (1e-4 for an
+    fp32 output) applies to the fp32 accumulation itself, on sampled rows against the
+    oracle."""
+    w = W.custom(8192, 8192, 8192, W.BF16, W.F32, b_layout, "none", ("uniform", -1.0, 1.0),
+                 name=f"{'nn' if b_layout == W.B_KN else 'tn'}_bf16_8192_f32out")
     _log(f"workload {w.name}: {w.describe()}")
     a, b = W.make_inputs(w)
     C, cfg = G.run(w, a, b)
