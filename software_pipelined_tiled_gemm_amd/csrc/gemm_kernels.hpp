@@ -248,7 +248,10 @@ __device__ __forceinline__ floatx16 mfma(const u32x4& x, const u32x4& y, const f
 // ---------------------------------------------------------------------------
 
 // Epilogue of one wave: accumulator -> (GELU / ReLU) -> output type -> LDS staging ->
-// 16-byte row-contiguous global stores.  The wave's C tile is processed in 32-row
+// 16-byte row-contiguous global stores.  The stores are nontemporal: C is written once
+// and never read here, and at the end of each round of tiles every workgroup stores its
+// tile at once (32 MiB at 8192^3), which with the default policy evicts A/B panel
+// lines the next round still needs (measured at 8192^3: NN -2.0%, TN -3.7% time).  The wave's C tile is processed in 32-row
 // blocks (one MFMA block row), NP blocks per round: a round writes its blocks into NP
 // private 32 x WN staging buffers, then reads them back row by row and stores them, so
 // the LDS write -> read -> store latency is paid once per round rather than per block.
@@ -320,7 +323,7 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TN][TM], char* 
                 if (gm < M && gn < N) {
                     char* dstg = (char*)args.C + ((size_t)gm * N + gn) * OB;
                     if (vec_ok && gn + E16 <= N) {
-                        *(u32x4*)dstg = val;
+                        __builtin_nontemporal_store(val, (u32x4*)dstg);
                     } else {
                         const int lim = (N - gn) < E16 ? (N - gn) : E16;
                         for (int e = 0; e < lim; ++e) {
@@ -397,7 +400,7 @@ __device__ __forceinline__ void store_tile16(const floatx4 (&acc)[TN][TM], char*
                 if (gm < M && gn < N) {
                     char* dstg = (char*)args.C + ((size_t)gm * N + gn) * OB;
                     if (vec_ok && gn + E16 <= N) {
-                        *(u32x4*)dstg = val;
+                        __builtin_nontemporal_store(val, (u32x4*)dstg);
                     } else {
                         const int lim = (N - gn) < E16 ? (N - gn) : E16;
                         for (int e = 0; e < lim; ++e) {
@@ -442,7 +445,7 @@ __device__ __forceinline__ void store_direct16(const AccV (&acc)[TN][TM], const 
                 if (gm < M && gn < N) {
                     uint16_t* dst = (uint16_t*)args.C + ((size_t)gm * N + gn);
                     if (vec_ok && gn + 4 <= N) {
-                        *(u32x2*)dst = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+                        __builtin_nontemporal_store(u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)}, (u32x2*)dst);
                     } else {
                         const int lim = (N - gn) < 4 ? (N - gn) : 4;
                         for (int e = 0; e < lim; ++e) dst[e] = (uint16_t)h[e];
