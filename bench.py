@@ -347,8 +347,9 @@ def parse_tile(spec):
 # distinct kernel instantiation, so a profiler run over `--ablations` attributes
 # counters to the rows by kernel name.
 ABLATIONS = [
-    ("default: 256x256x64, S=2, 8 waves of 128x64, direct copies, 16x16x32 MFMAs, group_m 4", "256x256x64:2:1:4:0:128x64:1:0:0:0:1:16"),
-    ("the same with group_m 8 (the 32x32x16 kernel's best)", "256x256x64:2:1:8:0:128x64:1:0:0:0:1:16"),
+    ("default: 256x256x64, 8 waves of 128x64, 16x16x32 MFMAs, B one slot deeper than A (staging 6), compiler-placed schedule, group_m 4", "256x256x64:2:1:4:6:128x64:1:1:0:0:1:16"),
+    ("the same with group_m 8 (the 32x32x16 kernel's best)", "256x256x64:2:1:8:6:128x64:1:1:0:0:1:16"),
+    ("two-slot ring (S=2), hand-placed schedule: the base of the 16x16x32 rows below", "256x256x64:2:1:4:0:128x64:1:0:0:0:1:16"),
     ("16x16x32, no swizzle", "256x256x64:2:0:4:0:128x64:1:0:0:0:1:16"),
     ("16x16x32, no overlap (S=1, the serial loop)", "256x256x64:1:1:4:0:128x64:1:0:0:0:1:16"),
     ("16x16x32, compiler-placed schedule", "256x256x64:2:1:4:0:128x64:1:1:0:0:1:16"),

@@ -90,6 +90,9 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1, GEMM_EPI_RELU = 2 } ge
  *                       4 = as 0, with A in a ring one slot deeper than B (stages =
  *                       2: three A slots, two B slots), so the copies of A have two
  *                       k-tiles to land and those of B one;
+ *                       6 = as 4 with the roles swapped: B in a ring one slot
+ *                       deeper than A (stages = 2: two A slots, three B slots);
+ *                       compiled with schedule = 1 (16x16x32 tiles);
  *                       5 = as 0, with a slot refilled one k-tile after its release
  *                       (the Pallas guide's release delay of 1; stages >= 3): S-1
  *                       k-tiles in flight instead of S
@@ -121,7 +124,8 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1, GEMM_EPI_RELU = 2 } ge
  *                       flops with half the accumulator register traffic per flop
  * The LDS a configuration needs is stages * (block_m + block_n) * block_k * 2 bytes
  * (the shared-memory bound of the TileLang tutorial's shared_bytes()), plus
- * block_m * block_k * 2 for staging 4, at most 160 KiB. */
+ * block_m * block_k * 2 for staging 4 or block_n * block_k * 2 for staging 6, at
+ * most 160 KiB. */
 typedef struct {
     int32_t block_m, block_n, block_k;
     int32_t stages;

@@ -26,7 +26,7 @@ DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
 B_LAYOUTS = {"kn": 0, "nk": 1}
 EPILOGUES = {"none": 0, "gelu_tanh": 1, "relu": 2}
 STAGING = {0: "direct", 1: "vgpr", 2: "direct-spread", 3: "producer-wave", 4: "direct-a-deep",
-           5: "direct-late-release"}
+           5: "direct-late-release", 6: "direct-b-deep"}
 
 
 class GemmError(RuntimeError):

@@ -132,12 +132,12 @@ bool pipelined_fits(int64_t M, int64_t N, int64_t K, gemm_b_layout bl) {
 }
 
 const Variant* find_cfg(int bm, int bn, int bk, int stages, int staging, int wm, int wn,
-                        int persistent = 0, int mfma = 32) {
+                        int persistent = 0, int mfma = 32, int schedule = 0) {
     for (const Variant& v : kVariants)
         if (v.cfg.block_m == bm && v.cfg.block_n == bn && v.cfg.block_k == bk &&
             v.cfg.stages == stages && v.cfg.staging == staging && v.cfg.swizzle == 1 &&
             v.cfg.wave_m == wm && v.cfg.wave_n == wn && v.cfg.lookahead == 1 &&
-            v.cfg.schedule == 0 && v.cfg.persistent == persistent && v.cfg.mfma == mfma)
+            v.cfg.schedule == schedule && v.cfg.persistent == persistent && v.cfg.mfma == mfma)
             return &v;
     return nullptr;
 }
@@ -155,7 +155,7 @@ int cu_count() {
     return n;
 }
 
-gemm_tile_config heuristic(int64_t M, int64_t N) {
+gemm_tile_config heuristic(int64_t M, int64_t N, gemm_b_layout bl) {
     // Estimated time of a candidate = rounds of the 256 CUs it needs x its tile's
     // area / its measured per-tile throughput relative to 256x256 (bf16 NN 8192^3
     // and the 1024x8192x8192 shard on MI355X: 256x128 runs at 0.91 of the 256x256
@@ -180,7 +180,17 @@ gemm_tile_config heuristic(int64_t M, int64_t N) {
         const double t = (double)((tiles + cus - 1) / cus) * c.bm * c.bn / c.eff;
         if (!best || t < best_t) { best = &c; best_t = t; }
     }
-    gemm_tile_config c = find_cfg(best->bm, best->bn, best->bk, best->st, 0, best->wm, best->wn, 0, best->mfma)->cfg;
+    // B stored [K,N] on grids of two rounds or more: the B-deep ring (staging 6, three B
+    // slots, compiler-placed schedule).  A [K,N] k-tile of B is 64 rows 2*N bytes apart,
+    // and its copies are the ones that land late: measured interleaved at 8192^3, bf16
+    // NN 710.0 -> 701.3 us, fp16 NN 753.6 -> 747.5 us; with B stored [N,K] it makes no
+    // difference (700.5 / 700.0 us).  Grids of one round keep the two-slot ring.
+    const int64_t tiles = ((M + best->bm - 1) / best->bm) * ((N + best->bn - 1) / best->bn);
+    const Variant* v = nullptr;
+    if (bl == GEMM_B_KN && best->bm == 256 && best->bn == 256 && tiles >= 2 * cus)
+        v = find_cfg(256, 256, 64, 2, 6, best->wm, best->wn, 0, 16, 1);
+    if (!v) v = find_cfg(best->bm, best->bn, best->bk, best->st, 0, best->wm, best->wn, 0, best->mfma);
+    gemm_tile_config c = v->cfg;
     // 4 tile rows per raster group: with the 16x16x32 tiles at 8192^3 (32 tile rows),
     // measured interleaved: group_m 2 / 4 / 8 / 16 / 32 = 758 / 730 / 740 / 752 / 911 us
     // (NN) and 765 / 733 /741 / 766 / 934 us (TN); the 32x32x16 kernel preferred 8
@@ -281,8 +291,10 @@ gemm_status gemm_list_config(int32_t index, gemm_tile_config* out) {
 int64_t gemm_lds_bytes(const gemm_tile_config* c) {
     if (!c) return -1;
     const int64_t ring = (int64_t)c->stages * ((int64_t)c->block_m + c->block_n) * c->block_k * 2;
-    // the A-deep ring holds one more k-tile of A
-    return c->staging == 4 ? ring + (int64_t)c->block_m * c->block_k * 2 : ring;
+    // the A-deep ring holds one more k-tile of A, the B-deep ring one more of B
+    if (c->staging == 4) return ring + (int64_t)c->block_m * c->block_k * 2;
+    if (c->staging == 6) return ring + (int64_t)c->block_n * c->block_k * 2;
+    return ring;
 }
 
 gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_dtype in_dtype,
@@ -304,7 +316,7 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
             force->stages <= 0 || force->wave_m <= 0 || force->wave_n <= 0 ||
             force->group_m < 0 || (force->swizzle != 0 && force->swizzle != 1) ||
             (force->xcd_remap != 0 && force->xcd_remap != 1) ||
-            force->staging < 0 || force->staging > 5 ||
+            force->staging < 0 || force->staging > 6 ||
             (force->store != 0 && force->store != 1) ||
             (force->mfma != 0 && force->mfma != 16 && force->mfma != 32) ||
             (force->lookahead != 1 && force->lookahead != 2) ||
@@ -327,7 +339,7 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
                 have = true;
             }
         }
-        if (!have) cfg = heuristic(M, N);
+        if (!have) cfg = heuristic(M, N, b_layout);
         var = find_variant(cfg);
         if (!var) return GEMM_ERR_INTERNAL;
     }

@@ -531,6 +531,12 @@ __device__ __forceinline__ int kswz_t(int r) {
 //      A copies of k-tile t+3 in flight.  With the tile raster's 8 x 4 blocks of
 //      tiles per XCD, A carries 2/3 of the bytes that miss L2.  The loop is unrolled
 //      by 6 k-tiles (three A slots x two B slots), plus an unrolled tail.
+//   6  the mirror of 4: B in a ring one slot deeper than A (two A slots, three B
+//      slots).  The window after barrier t copies A of k-tile t+2, then B of k-tile
+//      t+3, and the wait before barrier t+1 leaves the B copies in flight.  With the
+//      16x16x32 tiles it fits the registers only under the compiler's schedule
+//      (SCHED 1; the hand-placed one spills), and there it is the fastest measured
+//      configuration at bf16 8192^3 (NN -1.3% time against mode 0 hand-placed).
 //   5  direct-to-LDS copies as in 0, but a slot is refilled one k-tile after its
 //      release (the release delay of 1 in the Pallas guide's terms): the window
 //      after barrier t copies k-tile t+S-1 into the slot released at barrier t-1, so
@@ -573,6 +579,8 @@ pipelined_gemm(KArgs args) {
     static_assert(!PERS || (LDM == 0 && S >= 2), "persistent: direct copies and a ring of >= 2 slots");
     static_assert(LDM != 4 || (S == 2 && S * G::STAGE + G::A_BYTES <= 160 * 1024),
                   "A-deep ring: two slots plus one more A slot within the LDS");
+    static_assert(LDM != 6 || (S == 2 && S * G::STAGE + G::B_BYTES <= 160 * 1024),
+                  "B-deep ring: two slots plus one more B slot within the LDS");
     static_assert(LDM != 5 || S >= 3, "a late release needs a ring of three slots or more");
     static_assert(!PERS || S * G::STAGE + G::NW * 32 * WN * 2 <= 160 * 1024,
                   "persistent: ring + epilogue staging must fit the LDS");
@@ -589,10 +597,11 @@ pipelined_gemm(KArgs args) {
     __shared__ __attribute__((aligned(1024))) char ring4[S > 4 ? G::STAGE : 16];
     __shared__ __attribute__((aligned(1024))) char ring5[S > 5 ? G::STAGE : 16];
     __shared__ __attribute__((aligned(1024))) char ring_a2[LDM == 4 ? G::A_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char ring_b2[LDM == 6 ? G::B_BYTES : 16];
 
     // ring slot s as a compile-time choice of array (see the header comment); a slot
-    // is addressed through its A and B parts, which the A-deep ring (LDM 4) places in
-    // different arrays
+    // is addressed through its A and B parts, which the A-deep and B-deep rings (LDM 4
+    // and 6) place in different arrays
     struct Slot {
         SPG_LDS char* a;
         SPG_LDS char* b;
@@ -611,9 +620,17 @@ pipelined_gemm(KArgs args) {
         return Slot{r, r + G::A_BYTES};
     };
     // slot of k-tile t for t % 6 == i in the A-deep ring: A in the A part of ring0,
-    // ring1 or in ring_a2 (t % 3), B in the B part of ring0 or ring1 (t % 2)
+    // ring1 or in ring_a2 (t % 3), B in the B part of ring0 or ring1 (t % 2).  The
+    // B-deep ring (LDM 6) mirrors it: A in ring0/ring1 (t % 2), B in the B part of
+    // ring0, ring1 or in ring_b2 (t % 3)
     auto deep_slot = [&](auto ic) -> Slot {
         constexpr int i = decltype(ic)::value;
+        if constexpr (LDM == 6) {
+            SPG_LDS char* a = (i % 2) == 0 ? (SPG_LDS char*)ring0 : (SPG_LDS char*)ring1;
+            SPG_LDS char* b = (i % 3) == 0 ? (SPG_LDS char*)ring0 + G::A_BYTES
+                            : (i % 3) == 1 ? (SPG_LDS char*)ring1 + G::A_BYTES : (SPG_LDS char*)ring_b2;
+            return Slot{a, b};
+        }
         SPG_LDS char* a = (i % 3) == 0 ? (SPG_LDS char*)ring0
                         : (i % 3) == 1 ? (SPG_LDS char*)ring1 : (SPG_LDS char*)ring_a2;
         SPG_LDS char* b = ((i % 2) == 0 ? (SPG_LDS char*)ring0 : (SPG_LDS char*)ring1) + G::A_BYTES;
@@ -935,7 +952,7 @@ pipelined_gemm(KArgs args) {
 #endif
     constexpr int RPS = SPG_READS_PER_STEP;  // LDS reads issued per MFMA step
     constexpr int CPS = G::L / KSTEPS;       // copy ops per stage when spread over a window
-    static_assert(LDM == 0 || LDM == 4 || LDM == 5 || G::L % KSTEPS == 0, "copy ops must split evenly over the stages");
+    static_assert(LDM == 0 || LDM == 4 || LDM == 5 || LDM == 6 || G::L % KSTEPS == 0, "copy ops must split evenly over the stages");
     // One MFMA stage with its memory traffic interleaved: step i issues MFMA i of
     // `now`, then copy op i and RPS LDS reads of the next stage (into `nx`, from
     // `rslot` at k-step rkk).  Copy modes: 1, all L direct-to-LDS ops of the k-tile
@@ -967,7 +984,9 @@ pipelined_gemm(KArgs args) {
                 mfma_step(now.b[bn], now.a[bm], acc[bn][bm]);
             }
             if constexpr (MD == 1 && i % CSP == 0 && i / CSP < NCP) {
-                // the A-deep ring issues B before A (see LDM 4)
+                // the A-deep ring issues B before A, so that the wait before the next
+                // barrier can leave A's copies in flight; the B-deep ring keeps the
+                // order A, B and leaves B's
                 constexpr int j = LDM == 4 ? (J0 + i / CSP + A_DMA) % G::L : J0 + i / CSP;
                 dma_op(cslot, src, std::integral_constant<int, j>{}, NotFirst{});
             }
@@ -1017,7 +1036,7 @@ pipelined_gemm(KArgs args) {
     static_assert(KSTEPS % NF == 0, "fragment sets must tile the k-steps of a k-tile");
     Frags fr[NF];
     auto fset = [&](auto ic) -> Frags& { return fr[decltype(ic)::value % NF]; };
-    constexpr bool DIRECT = LDM == 0 || LDM == 4 || LDM == 5;  // all copies of a window right after its barrier
+    constexpr bool DIRECT = LDM == 0 || LDM == 4 || LDM == 5 || LDM == 6;  // all copies of a window right after its barrier
     using ModeWin = std::integral_constant<int, DIRECT ? 1 : (LDM == 1 ? 2 : 3)>;
     constexpr int WOPS = DIRECT ? G::L / PF : CPS;    // copy ops per window stage
     static_assert(!DIRECT || G::L % PF == 0, "copies must split over the lookahead stages");
@@ -1076,6 +1095,15 @@ pipelined_gemm(KArgs args) {
                 dma_op(deep_slot(std::integral_constant<int, 2>{}), src, jc, NotFirst{});
             });
             wait_vmcnt<G::L + A_DMA>();
+        } else if constexpr (LDM == 6) {
+            // prologue: k-tiles 0 and 1, and B of k-tile 2; wait for k-tile 0
+            issue(deep_slot(Z_{}), 0, First{});
+            issue(deep_slot(std::integral_constant<int, 1>{}), 1, NotFirst{});
+            const DmaSrc src = dma_src(2);
+            static_for<A_DMA, G::L>([&](auto jc) {
+                dma_op(deep_slot(std::integral_constant<int, 2>{}), src, jc, NotFirst{});
+            });
+            wait_vmcnt<G::L + B_DMA>();
         } else if constexpr (LDM == 5) {
             // prologue: k-tiles 0 .. S-2 (slot S-1 is filled by the first window); wait
             // for k-tile 0
@@ -1113,16 +1141,16 @@ pipelined_gemm(KArgs args) {
         static_for<0, PF>([&](auto kc) { load_frags(slot_of(Z_{}), kc.value, fset(kc)); });
 
         // outstanding copies allowed at the wait before barrier t: k-tiles t+2 .. t+S-1
-        // (and, in the A-deep ring, A of k-tile t+2)
-        constexpr int STEADY = LDM == 4 ? A_DMA : (LDM == 5 ? (S - 3) * G::L : (S - 2) * G::L);
+        // (in the A-deep ring, A of k-tile t+2; in the B-deep ring, B of k-tile t+2)
+        constexpr int STEADY = LDM == 4 ? A_DMA : LDM == 6 ? B_DMA : (LDM == 5 ? (S - 3) * G::L : (S - 2) * G::L);
         auto ktile = [&](auto sc, int t) __attribute__((always_inline)) {
             constexpr int s = decltype(sc)::value;
-            // slots of k-tiles t-1, t, t+1 (s = t mod S, or t mod 6 in the A-deep ring)
+            // slots of k-tiles t-1, t, t+1 (s = t mod S, or t mod 6 in the deep rings)
             auto slot_at = [&](auto ic) -> Slot {
-                if constexpr (LDM == 4) return deep_slot(std::integral_constant<int, decltype(ic)::value % 6>{});
+                if constexpr (LDM == 4 || LDM == 6) return deep_slot(std::integral_constant<int, decltype(ic)::value % 6>{});
                 else return slot_of(std::integral_constant<int, decltype(ic)::value % S>{});
             };
-            constexpr int NS = LDM == 4 ? 6 : S;
+            constexpr int NS = (LDM == 4 || LDM == 6) ? 6 : S;
             const Slot cur = slot_at(sc);
             const Slot prev = slot_at(std::integral_constant<int, (s + NS - 1) % NS>{});
             const Slot nxt = slot_at(std::integral_constant<int, (s + 1) % NS>{});
@@ -1162,6 +1190,7 @@ pipelined_gemm(KArgs args) {
                 const auto src = [&]() __attribute__((always_inline)) {
                     if constexpr (PERS) return next_copy();
                     else if constexpr (LDM == 4) return DmaSrc{dma_src(t + 3).a, dma_src(t + 2).b};
+                    else if constexpr (LDM == 6) return DmaSrc{dma_src(t + 2).a, dma_src(t + 3).b};
                     else if constexpr (LDM == 5) return dma_src(t + S - 1);
                     else return src_of(LDM == 1 ? t + S + 1 : t + S);
                 }();
@@ -1198,7 +1227,7 @@ pipelined_gemm(KArgs args) {
             for (int t0 = 0; t0 < ns; t0 += S) {
                 static_for<0, S>([&](auto sc) { ktile(sc, t0 + decltype(sc)::value); });
             }
-        } else if constexpr (LDM == 4) {
+        } else if constexpr (LDM == 4 || LDM == 6) {
             // six k-tiles per iteration (the slot pattern repeats every 6), then the
             // remaining nk % 6 one by one: no k-tile past nk is multiplied
             int t0 = 0;

@@ -132,12 +132,25 @@ def test_forced_configs(L):
         spg.gemm_create(512, 512, 512, force=sto)
     assert e.value.status == 1
     # release delay 1 (staging 5) needs a ring of three slots; the A-deep ring (staging 4)
-    # holds one more k-tile of A than the TileLang budget formula counts
+    # holds one more k-tile of A than the TileLang budget formula counts, the B-deep ring
+    # (staging 6) one more of B
+    deep = set()
     for i in range(n):
         c = spg.gemm_list_config(i)
         assert c.staging != 5 or c.stages >= 3
         if c.staging == 4:
             assert spg.gemm_lds_bytes(c) == (c.stages * (c.block_m + c.block_n) + c.block_m) * c.block_k * 2
+        if c.staging == 6:
+            assert spg.gemm_lds_bytes(c) == (c.stages * (c.block_m + c.block_n) + c.block_n) * c.block_k * 2
+        if c.staging in (4, 6):
+            deep.add(c.staging)
+            assert c.stages == 2 and spg.gemm_lds_bytes(c) <= 160 * 1024
+    assert deep == {4, 6}
+    bad_staging = spg.TileConfig(block_m=256, block_n=256, block_k=64, stages=2, wave_m=128,
+                                 wave_n=64, swizzle=1, group_m=4, xcd_remap=1, staging=7)
+    with pytest.raises(spg.GemmError) as e:
+        spg.gemm_create(512, 512, 512, force=bad_staging)
+    assert e.value.status == 1
     for look in (0, 3):
         far = spg.TileConfig(block_m=256, block_n=256, block_k=64, stages=2, wave_m=128,
                              wave_n=128, swizzle=1, group_m=4, xcd_remap=1, lookahead=look)
@@ -198,7 +211,15 @@ def test_heuristic_tiles(L):
         return c
     big = cfg(8192, 8192, 8192)
     assert (big.block_m, big.block_n, big.wave_m, big.wave_n) == (256, 256, 128, 64)
-    assert (big.mfma, big.staging) == (16, 0)     # 16x16x32 MFMAs on the 8-wave tiles
+    # 16x16x32 MFMAs on the 8-wave tiles; B stored [K,N] on a grid of several rounds:
+    # the B-deep ring under the compiler's schedule
+    assert (big.mfma, big.staging, big.schedule) == (16, 6, 1)
+    h = spg.gemm_create(8192, 8192, 8192, "bf16", "bf16", "nk")
+    tn = spg.gemm_get_config(h)
+    spg.gemm_destroy(h)
+    assert (tn.block_m, tn.block_n, tn.mfma, tn.staging, tn.schedule) == (256, 256, 16, 0, 0)
+    one_round = cfg(4096, 4096, 4096)
+    assert (one_round.staging, one_round.schedule) == (0, 0)
     assert cfg(1024, 8192, 8192).mfma == 16 and cfg(256, 256, 256).mfma == 32
     small = cfg(256, 256, 256)
     assert (small.block_m, small.block_n) == (128, 128)

@@ -296,12 +296,14 @@ def test_persistent_falls_back_where_it_does_not_apply():
         assert np.array_equal(G.c_values(C2, w), got)
 
 
-def test_a_deep_ring_every_tail():
-    # the A-deep ring runs six k-tiles per iteration and then the rest one by one: every
-    # remainder 0..5, fewer k-tiles than one iteration, a leading partial k-tile, both
-    # layouts; bitwise equal to the two-deep ring (same k order) and within tolerance
-    deep = [c for c in _variants() if c.staging == 4 and c.mfma == 32]
-    assert deep, "no A-deep configuration compiled"
+@pytest.mark.parametrize("staging", [4, 6], ids=["a_deep", "b_deep"])
+def test_deep_ring_every_tail(staging):
+    # the A-deep (B-deep) ring runs six k-tiles per iteration and then the rest one by
+    # one: every remainder 0..5, fewer k-tiles than one iteration, a leading partial
+    # k-tile, both layouts; bitwise equal to the two-deep ring of the same tile, MFMA
+    # shape and schedule (same k order) and within tolerance
+    deep = [c for c in _variants() if c.staging == staging]
+    assert deep, f"no staging-{staging} configuration compiled"
     d = deep[0]
     twin = [c for c in _variants() if c.staging == 0 and (c.block_m, c.block_n, c.block_k, c.stages,
             c.wave_m, c.wave_n, c.lookahead, c.schedule, c.persistent, c.mfma) ==
@@ -311,9 +313,9 @@ def test_a_deep_ring_every_tail():
         for layout in (W.B_KN, W.B_NK):
             w = W.custom(300, 520, K, W.BF16, W.BF16, layout, "none", ("uniform", -1.0, 1.0))
             a, b = W.make_inputs(w)
-            _log(f"a-deep K={K} {w.describe()}")
+            _log(f"staging {staging} K={K} {w.describe()}")
             C, used = G.run(w, a, b, force=d)
-            assert used.staging == 4
+            assert used.staging == staging
             got = G.c_values(C, w)
             G.check(w, a, b, got)
             C2, _ = G.run(w, a, b, force=twin)
