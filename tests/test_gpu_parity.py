@@ -322,6 +322,27 @@ def test_deep_ring_every_tail(staging):
             assert np.array_equal(G.c_values(C2, w), got)
 
 
+def test_b_deep_ring_epilogues_and_outputs():
+    # the default kernel for B stored [K,N] on large grids: every output type and
+    # epilogue on a ragged shape, against the oracle and bitwise against its two-slot twin
+    deep = [c for c in _variants() if c.staging == 6][0]
+    twin = [c for c in _variants() if c.staging == 0 and (c.block_m, c.block_n, c.block_k, c.stages,
+            c.wave_m, c.wave_n, c.lookahead, c.schedule, c.mfma) ==
+            (deep.block_m, deep.block_n, deep.block_k, deep.stages, deep.wave_m, deep.wave_n,
+             deep.lookahead, deep.schedule, deep.mfma)][0]
+    for in_dtype, out_dtype, epi, K in ((W.BF16, W.F32, "gelu_tanh", 760), (W.F16, W.F16, "relu", 448),
+                                        (W.BF16, W.BF16, "gelu_tanh", 1000)):
+        w = W.custom(600, 776, K, in_dtype, out_dtype, W.B_KN, epi, ("uniform", -1.0, 1.0))
+        a, b = W.make_inputs(w)
+        _log(f"b-deep {w.describe()}")
+        C, used = G.run(w, a, b, force=deep)
+        assert used.staging == 6
+        got = G.c_values(C, w)
+        G.check(w, a, b, got)
+        C2, _ = G.run(w, a, b, force=twin)
+        assert np.array_equal(G.c_values(C2, w), got)
+
+
 def test_autotune_keeps_parity():
     w = W.custom(1024, 768, 512, W.F16, W.F16, W.B_NK)
     a, b = W.make_inputs(w)
