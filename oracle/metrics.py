@@ -28,12 +28,15 @@ _EMIN = {"f16": -14, "bf16": -126, "f32": -126}
 
 
 def ulp(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Spacing of the output format at |x| (binade-wise; subnormal spacing below)."""
+    """Spacing of the output format at |x|: 2^(e - p) for |x| in the binade [2^e, 2^(e+1)),
+    p the format's fraction bits; the subnormal spacing 2^(emin - p) below the normal range
+    and at zero.  The binade comes from frexp, which is exact (a floor of log2 rounds up
+    into the next binade just below a power of two)."""
     ax = np.abs(np.asarray(x, dtype=np.float64))
-    with np.errstate(divide="ignore"):
-        e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
-    e = np.maximum(e, _EMIN[dtype])
-    return np.exp2(e - _FBITS[dtype])
+    _, e = np.frexp(ax)                     # ax = f 2^e with 0.5 <= f < 1: binade e - 1
+    b = np.where(ax > 0, e.astype(np.float64) - 1.0, float(_EMIN[dtype]))
+    b = np.maximum(b, _EMIN[dtype])
+    return np.exp2(b - _FBITS[dtype])
 
 
 def scale(K: int, max_abs_a: float, max_abs_b: float) -> float:
