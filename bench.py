@@ -1,11 +1,16 @@
-"""Benchmark: GEMM TFLOP/s of the pipelined MFMA kernel at 8192^3 on one MI355X.
+"""Benchmark: GEMM TFLOP/s of the pipelined MFMA kernel at 8192^3 on one MI355X, and the
+fraction of the dense fp16/bf16 MFMA peak.
 
-Workload (one "step" = one GEMM over resident inputs): M = N = K = 8192, bf16 A
-[M,K] and B [K,N] row-major (NN), entries uniform [-1, 1] from seeds 42/43,
-fp32 accumulation, bf16 output.  The same problem in fp16 is timed too and
-reported under "extra".  Prints one JSON line.
+Headline workload (one "step" = one GEMM over inputs already resident in HBM): fp16
+M = N = K = 8192, A [M,K] and B [K,N] row-major (NN), entries uniform [-1, 1] from seeds
+42/43, fp32 accumulation, fp16 output -- the metric names fp16 8192^3; layout and inputs
+are those of the 8192^3 configuration, which is bf16 and is reported under "extra"
+beside every other configuration (256^3, 4096^3, 3000x5000x1000 with masked tails,
+3072x4096x4096 with the fused GELU), each with its roofline and its oracle on the host.
+Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps 200] [--warmup 500] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps 200] [--warmup 500] [--min-warmup-s 1.0]
+                  [--no-cpu-baseline] [--no-extra]
 """
 
 from __future__ import annotations
@@ -13,6 +18,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -22,15 +28,60 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense MFMA, published
 HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20                            # MI355X Infinity Cache (last level)
 METRIC = "GEMM TFLOP/s at fp16 8192³ on 1 MI355X; % of dense MFMA peak"
+HEADLINE = "nn_f16_8192"
+
+# The configurations reported under "extra", each with its roofline (the 8192^3 bf16
+# configuration first); the 256^3 one is a launch-latency case, not a roofline one.
+CONFIG_LINES = ["nn_bf16_8192", "tn_f16_256", "tn_f16_4096", "tn_f16_3000x5000x1000_f32out",
+                "nn_bf16_3072x4096x4096_gelu"]
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def time_gemm(w, steps, warmup, force=None):
-    """Returns (ms_per_step wall, kernel ms from HIP events on the launch stream, config)."""
+def warm_up(fn, launches, min_s, sync):
+    """Run fn() at least `launches` times and for at least `min_s` seconds of back-to-back
+    work (the GPU leaves its idle clock state over the first ~0.1-0.3 s); returns the
+    launches and seconds actually run."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < launches:
+        fn()
+        n += 1
+    sync()
+    while time.perf_counter() - t0 < min_s:
+        for _ in range(10):
+            fn()
+        n += 10
+        sync()
+    return n, time.perf_counter() - t0
+
+
+def timed_launches(fn, steps, stream, sync):
+    """Time `steps` launches back to back with HIP events recorded on the launch stream
+    (torch's events wrap hipEventRecord): one event before the first launch and one after
+    each, so the window mean (the whole job) and every launch's own interval are known."""
+    import torch
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    sync()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    sync()
+    wall = (time.perf_counter() - t0) / steps
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return {"mean_ms": ev[0].elapsed_time(ev[steps]) / steps, "median_ms": statistics.median(per),
+            "min_ms": min(per), "wall_ms": wall * 1e3}
+
+
+def time_gemm(w, steps, warmup, force=None, min_warmup_s=0.0):
+    """Times the GEMM of workload w (resident inputs); returns (timing dict, config)."""
     import numpy as np
     import torch
 
@@ -44,29 +95,40 @@ def time_gemm(w, steps, warmup, force=None):
     C = torch.empty((w.M, w.N), dtype=torch.int16 if w.out_dtype != W.F32 else torch.float32,
                     device=dev)
     stream = torch.cuda.current_stream(dev)
+    sync = lambda: torch.cuda.synchronize(dev)
     g = spg.Gemm(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.b_layout, w.epilogue, force)
     cfg = g.config()
-    for _ in range(warmup):
-        g(A, B, C, stream)
-    torch.cuda.synchronize(dev)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
-        g(A, B, C, stream)
-    e1.record(stream)
-    torch.cuda.synchronize(dev)
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    kern_ms = e0.elapsed_time(e1) / steps
+    run = lambda: g(A, B, C, stream)
+    n_warm, s_warm = warm_up(run, warmup, min_warmup_s, sync)
+    t = timed_launches(run, steps, stream, sync)
+    t.update(warmup_launches_run=n_warm, warmup_s=round(s_warm, 3))
     g.close()
     del A, B, C
     torch.cuda.empty_cache()
-    return wall_ms, kern_ms, cfg
+    return t, cfg
+
+
+def gemm_line(w, t, cfg):
+    """One configuration's line: times (window mean, per-launch median and minimum), TFLOP/s
+    and its MFMA roofline."""
+    import workloads as W
+
+    tf = w.flops / (t["mean_ms"] * 1e-3) / 1e12
+    algo = 2 * (w.M * w.K + w.K * w.N) + (4 if w.out_dtype == W.F32 else 2) * w.M * w.N
+    return {"M": w.M, "N": w.N, "K": w.K, "in_dtype": w.in_dtype, "out_dtype": w.out_dtype,
+            "b_layout": w.b_layout, "epilogue": w.epilogue,
+            "kernel_us_mean": round(t["mean_ms"] * 1e3, 2),
+            "kernel_us_median": round(t["median_ms"] * 1e3, 2),
+            "kernel_us_min": round(t["min_ms"] * 1e3, 2),
+            "tflops": round(tf, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_TFLOPS[w.in_dtype],
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_TFLOPS[w.in_dtype], 4),
+                         "traffic": measured_traffic(w.name, cfg, w), "algorithmic_bytes": algo},
+            "config": cfg.as_dict()}
 
 
 def time_gelu(n, dtype, steps, warmup):
-    """Mean kernel time (ms) of the standalone GELU over n resident elements."""
+    """Per-launch timing of the standalone GELU over n resident elements."""
     import numpy as np
     import torch
 
@@ -78,17 +140,13 @@ def time_gelu(n, dtype, steps, warmup):
     X = torch.from_numpy(x.view(np.int16)).to(dev)
     Y = torch.empty_like(X)
     stream = torch.cuda.current_stream(dev)
-    for _ in range(warmup):
-        spg.gelu_run(X, Y, n, dtype, stream)
-    torch.cuda.synchronize(dev)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        spg.gelu_run(X, Y, n, dtype, stream)
-    e1.record(stream)
-    torch.cuda.synchronize(dev)
-    return e0.elapsed_time(e1) / steps
+    sync = lambda: torch.cuda.synchronize(dev)
+    run = lambda: spg.gelu_run(X, Y, n, dtype, stream)
+    warm_up(run, warmup, 0.0, sync)
+    t = timed_launches(run, steps, stream, sync)
+    del X, Y
+    torch.cuda.empty_cache()
+    return t
 
 
 def copy_rate(nbytes, steps, warmup):
@@ -109,35 +167,68 @@ def copy_rate(nbytes, steps, warmup):
         b.copy_(a)
     e1.record()
     torch.cuda.synchronize(dev)
-    return 2 * nbytes / (e0.elapsed_time(e1) / steps * 1e-3) / 1e9
+    rate = 2 * nbytes / (e0.elapsed_time(e1) / steps * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return rate
 
 
 def gelu_lines(steps, warmup):
-    """The standalone GELU on the XLA page's bf16 [6,512,4096] tensor (HBM roofline), and
-    the GELU'd GEMM of that shape fused (epilogue) against unfused (GEMM, then GELU)."""
+    """The standalone GELU on the XLA page's bf16 [6,512,4096] tensor, whose 50 MB of
+    input and output stay in the 256 MB Infinity Cache across back-to-back launches (so
+    its rate is not an HBM figure), and on a tensor 16 times larger (805 MB moved per
+    launch, far beyond that cache: the HBM roofline); then the GELU'd GEMM of that shape
+    fused (epilogue) against unfused (GEMM, then GELU)."""
     import workloads as W
 
-    n = 6 * 512 * 4096
-    ms = time_gelu(n, "bf16", steps, warmup)
-    gbs = 2 * n * 2 / (ms * 1e-3) / 1e9
-    copy_gbs = copy_rate(2 * n, steps, warmup)
-    out = {"gelu_bf16_6x512x4096": {
-        "kernel_us": round(ms * 1e3, 2), "GB_per_s": round(gbs, 1),
-        "device_copy_same_bytes_GB_per_s": round(copy_gbs, 1),
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "algorithmic_bytes": 4 * n}}}
+    out = {}
+    for name, n in (("gelu_bf16_6x512x4096", 6 * 512 * 4096),
+                    ("gelu_bf16_16x6x512x4096", 16 * 6 * 512 * 4096)):
+        t = time_gelu(n, "bf16", steps, warmup)
+        moved = 2 * n * 2
+        gbs = moved / (t["mean_ms"] * 1e-3) / 1e9
+        resident = moved <= MALL_BYTES
+        out[name] = {
+            "elements": n, "kernel_us_mean": round(t["mean_ms"] * 1e3, 2),
+            "kernel_us_median": round(t["median_ms"] * 1e3, 2), "GB_per_s": round(gbs, 1),
+            "device_copy_same_bytes_GB_per_s": round(copy_rate(moved // 2, steps, warmup), 1),
+            "working_set": ("in + out fit the 256 MB Infinity Cache: cache-resident, not an "
+                            "HBM figure" if resident else "in + out exceed the 256 MB Infinity "
+                            "Cache: streamed from HBM")}
+        if not resident:
+            out[name]["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                     "algorithmic_bytes": moved}
+        log(f"  {name}: {out[name]}")
     wf = W.WORKLOADS["nn_bf16_3072x4096x4096_gelu"]
     wp = W.custom(wf.M, wf.N, wf.K, wf.in_dtype, wf.out_dtype, wf.b_layout, "none", wf.dist,
                   name="nn_bf16_3072x4096x4096")
-    _, k_fused, _ = time_gemm(wf, steps, warmup)
-    _, k_plain, _ = time_gemm(wp, steps, warmup)
-    k_gelu = time_gelu(wf.M * wf.N, "bf16", steps, warmup)
+    t_fused, _ = time_gemm(wf, steps, warmup)
+    t_plain, _ = time_gemm(wp, steps, warmup)
+    t_gelu = time_gelu(wf.M * wf.N, "bf16", steps, warmup)
+    k_f, k_p, k_g = t_fused["mean_ms"], t_plain["mean_ms"], t_gelu["mean_ms"]
     out["gemm_gelu_3072x4096x4096"] = {
-        "fused_us": round(k_fused * 1e3, 2), "gemm_us": round(k_plain * 1e3, 2),
-        "gelu_us": round(k_gelu * 1e3, 2), "unfused_us": round((k_plain + k_gelu) * 1e3, 2),
-        "fused_tflops": round(wf.flops / (k_fused * 1e-3) / 1e12, 2)}
+        "fused_us": round(k_f * 1e3, 2), "gemm_us": round(k_p * 1e3, 2),
+        "gelu_us": round(k_g * 1e3, 2), "unfused_us": round((k_p + k_g) * 1e3, 2),
+        "fused_tflops": round(wf.flops / (k_f * 1e-3) / 1e12, 2)}
     return out
+
+
+def cliff_line(steps, warmup):
+    """K % 8 != 0 against its K % 8 == 0 neighbour (3000x5000x1001 / x1000, fp16, B [N,K],
+    fp32 output): rows of A and B that are not 16-byte aligned."""
+    import workloads as W
+
+    base = W.WORKLOADS["tn_f16_3000x5000x1000_f32out"]
+    odd = W.custom(base.M, base.N, 1001, base.in_dtype, base.out_dtype, base.b_layout,
+                   base.epilogue, base.dist, name="tn_f16_3000x5000x1001_f32out")
+    t_odd, cfg_odd = time_gemm(odd, steps, warmup)
+    t_base, _ = time_gemm(base, steps, warmup)
+    return {"K": 1001, "kernel_us_mean": round(t_odd["mean_ms"] * 1e3, 2),
+            "tflops": round(odd.flops / (t_odd["mean_ms"] * 1e-3) / 1e12, 2),
+            "neighbour_K1000_us_mean": round(t_base["mean_ms"] * 1e3, 2),
+            "time_ratio_to_neighbour": round(t_odd["mean_ms"] / t_base["mean_ms"], 3),
+            "config": cfg_odd.as_dict()}
 
 
 def _socket_power_w():
@@ -171,7 +262,7 @@ def _power_cap_w():
 def sustained_clock(w, seconds=3.0):
     """Runs the workload back to back for `seconds` while sampling the engine clock
     (rocm-smi) and the socket power (amd-smi) the SMU reports; returns (median MHz,
-    kernel us at that time, median socket W or None) or None."""
+    kernel us over the run, median socket W or None) or None."""
     import json as _json
     import subprocess
     import threading
@@ -226,6 +317,8 @@ def sustained_clock(w, seconds=3.0):
     stop.set()
     th.join()
     g.close()
+    del A, B, C
+    torch.cuda.empty_cache()
     us = e0.elapsed_time(e1) * 1e3 / n
     if len(samples) < 3:
         return None
@@ -234,8 +327,19 @@ def sustained_clock(w, seconds=3.0):
     return samples[len(samples) // 2], us, (watts[len(watts) // 2] if watts else None)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, target_s=15.0):
-    """The oracle (fp64 triple loop, OpenMP over rows) on a bounded sample of rows."""
+    """The oracle (fp64 triple loop, OpenMP over rows), untuned, on a bounded sample of
+    rows of the workload, sized for about target_s seconds."""
     import numpy as np
 
     import oracle
@@ -252,16 +356,18 @@ def cpu_baseline(w, target_s=15.0):
         return time.perf_counter() - t0
 
     # two-point calibration separates the fixed cost (decoding B) from the per-row cost
-    r1, r2 = nt, 4 * nt
-    t1, t2 = run(r1), run(r2)
-    per_row = max((t2 - t1) / (r2 - r1), 1e-6)
+    r1, r2 = min(nt, w.M), min(4 * nt, w.M)
+    t1 = run(r1)
+    t2 = run(r2) if r2 > r1 else t1
+    per_row = max((t2 - t1) / (r2 - r1), 1e-6) if r2 > r1 else max(t1 / r1, 1e-6)
     rows = int(min(w.M, max(r2, (target_s - t1 + r1 * per_row) / per_row)))
-    rows = max(nt, rows - rows % nt)
+    rows = max(min(nt, w.M), rows - rows % nt if rows >= nt else rows)
     dt = run(rows)
     flops = 2.0 * rows * w.N * w.K
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": o.num_threads(),
-            "kind": "oracle",
-            "sample": f"{rows} of {w.M} rows of C (all {w.N} columns, K={w.K}), {dt:.1f} s"}
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"{rows} of {w.M} rows of C (all {w.N} columns, K={w.K}), {dt:.1f} s "
+                      f"(B decoded once per call, included)"}
 
 
 KERNEL_SOURCE = os.path.join(ROOT, "software_pipelined_tiled_gemm_amd", "csrc", "gemm_kernels.hpp")
@@ -402,8 +508,10 @@ def run_ablations(w, steps, warmup):
     rows = []
     for label, spec in ablations_for(w.name):
         cfg = parse_tile(spec)
-        _, k, used = time_gemm(w, steps, warmup, cfg)
+        t, used = time_gemm(w, steps, warmup, cfg)
+        k = t["mean_ms"]
         rows.append({"label": label, "tile": spec, "kernel_us": round(k * 1e3, 2),
+                     "kernel_us_median": round(t["median_ms"] * 1e3, 2),
                      "tflops": round(w.flops / (k * 1e-3) / 1e12, 2)})
         log(f"  {label}: {rows[-1]['kernel_us']} us, {rows[-1]['tflops']} TFLOP/s")
     print(json.dumps({"ablations": rows, "workload": w.name, "steps": steps, "warmup": warmup}),
@@ -413,19 +521,20 @@ def run_ablations(w, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the GPU leaves its idle clock state over the first ~0.1-0.3 s of work: the
-    # default warm-up (500 launches, ~0.4 s at 8192^3) lets it settle first
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=500)
+    # the GPU leaves its idle clock state over the first ~0.1-0.3 s of work: the warm-up
+    # runs at least this long whatever --warmup says (the launches run are reported)
+    ap.add_argument("--min-warmup-s", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="nn_bf16_8192",
-                    help="workload name from workloads.WORKLOADS")
+    ap.add_argument("--workload", default=HEADLINE, help="workload name from workloads.WORKLOADS")
     ap.add_argument("--tile", default=None,
                     help="force a configuration: BMxBNxBK:S[:swizzle[:group_m[:staging[:WMxWN[:lookahead[:schedule[:persistent[:store[:xcd_remap[:mfma]]]]]]]]]] "
                          "(default: the library's choice)")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the extra lines (fp16 8192^3, the 8-GPU shard, the standalone "
-                         "GELU, fused vs unfused GELU GEMM, the sustained clock)")
+                    help="skip the extra lines (every other configuration, the 8-GPU shard, the "
+                         "K % 8 != 0 neighbour, the standalone GELU, fused vs unfused GELU GEMM, "
+                         "the sustained clock)")
     ap.add_argument("--ablations", action="store_true",
                     help="time the design-choice ablations on the workload instead of the "
                          "benchmark line (ABLATIONS, or the workload's own list in "
@@ -453,62 +562,76 @@ def main():
         run_ablations(w, args.steps, args.warmup)
         return
     force = parse_tile(args.tile) if args.tile else None
-    wall_ms, kern_ms, cfg = time_gemm(w, args.steps, args.warmup, force)
-    tflops = w.flops / (kern_ms * 1e-3) / 1e12
-    wall_tflops = w.flops / (wall_ms * 1e-3) / 1e12
-    log(f"  {cfg}: kernel {kern_ms * 1e3:.1f} us ({tflops:.1f} TFLOP/s), "
-        f"wall {wall_ms * 1e3:.1f} us/step")
+    t, cfg = time_gemm(w, args.steps, args.warmup, force, args.min_warmup_s)
+    head = gemm_line(w, t, cfg)
+    tflops = head["tflops"]
+    log(f"  {cfg}: kernel {head['kernel_us_mean']} us mean, {head['kernel_us_median']} median, "
+        f"{head['kernel_us_min']} min ({tflops} TFLOP/s); warm-up {t['warmup_launches_run']} "
+        f"launches in {t['warmup_s']} s")
 
     extra = {}
-    if args.workload == "nn_bf16_8192" and not args.no_extra:
-        w16 = W.WORKLOADS["nn_f16_8192"]
-        _, k16, cfg16 = time_gemm(w16, args.steps, args.warmup)
-        extra["nn_f16_8192"] = {"tflops": round(w16.flops / (k16 * 1e-3) / 1e12, 2),
-                                "kernel_us": round(k16 * 1e3, 2), "config": cfg16.as_dict()}
-        log(f"  fp16 8192^3: {extra['nn_f16_8192']}")
+    if args.workload == HEADLINE and not args.no_extra:
+        steps = max(args.steps, 50)
+        for name in CONFIG_LINES:
+            wc = W.WORKLOADS[name]
+            small = wc.flops < 1e9
+            tc, cc = time_gemm(wc, 200 if small else steps, args.warmup, None,
+                               0.2 if small else args.min_warmup_s)
+            extra[name] = gemm_line(wc, tc, cc)
+            if small:
+                extra[name]["note"] = ("4 tiles on 256 CUs: launch and latency bound, the "
+                                       "roofline fraction is not meaningful here")
+            if not args.no_cpu_baseline:
+                extra[name]["cpu_baseline"] = cpu_baseline(wc, 2.0 if name != "nn_bf16_8192" else 6.0)
+            log(f"  {name}: {extra[name]}")
         # one GPU's share of the 8-GPU row split (A and C by rows, B replicated)
-        wsh = W.custom(w.M // 8, w.N, w.K, w.in_dtype, w.out_dtype, w.b_layout, w.epilogue,
-                       name="nn_bf16_8192_shard_of_8")
-        _, ksh, cfgsh = time_gemm(wsh, args.steps, args.warmup)
-        extra[wsh.name] = {"M": wsh.M, "N": wsh.N, "K": wsh.K,
-                           "tflops": round(wsh.flops / (ksh * 1e-3) / 1e12, 2),
-                           "kernel_us": round(ksh * 1e3, 2), "config": cfgsh.as_dict()}
+        src = W.WORKLOADS["nn_bf16_8192"]
+        wsh = W.custom(src.M // 8, src.N, src.K, src.in_dtype, src.out_dtype, src.b_layout,
+                       src.epilogue, src.dist, name="nn_bf16_8192_shard_of_8")
+        tsh, csh = time_gemm(wsh, steps, args.warmup)
+        extra[wsh.name] = gemm_line(wsh, tsh, csh)
         log(f"  shard of 8: {extra[wsh.name]}")
-        extra.update(gelu_lines(args.steps, min(args.warmup, 200)))
-        log(f"  gelu: {extra['gelu_bf16_6x512x4096']}")
+        extra["k_not_multiple_of_8"] = cliff_line(steps, args.warmup)
+        log(f"  K % 8 != 0: {extra['k_not_multiple_of_8']}")
+        extra.update(gelu_lines(steps, min(args.warmup, 200)))
         log(f"  fused vs unfused GELU GEMM: {extra['gemm_gelu_3072x4096x4096']}")
-        clk = sustained_clock(w)
-        if clk is not None:
-            mhz, us, watts = clk
-            tf = w.flops / (us * 1e-6) / 1e12
-            extra["sustained_clock"] = {
-                "sclk_mhz_median": mhz, "kernel_us": round(us, 2), "tflops": round(tf, 2),
-                "mfma_busy_at_that_clock": round(tf / (PEAK_TFLOPS[w.in_dtype] * mhz / 2400.0), 4),
-                "socket_power_w_median": watts, "package_power_cap_w": _power_cap_w(),
-                "note": "3 s back-to-back run; clock (rocm-smi) and socket power (amd-smi) sampled "
-                        "while it runs; peak scales with clock"}
-            log(f"  sustained: {extra['sustained_clock']}")
+        for name in (HEADLINE, "nn_bf16_8192"):
+            wc = W.WORKLOADS[name]
+            clk = sustained_clock(wc)
+            if clk is not None:
+                mhz, us, watts = clk
+                tf = wc.flops / (us * 1e-6) / 1e12
+                extra[f"sustained_clock_{name}"] = {
+                    "sclk_mhz_median": mhz, "kernel_us": round(us, 2), "tflops": round(tf, 2),
+                    "frac_of_peak": round(tf / PEAK_TFLOPS[wc.in_dtype], 4),
+                    "mfma_busy_at_that_clock": round(tf / (PEAK_TFLOPS[wc.in_dtype] * mhz / 2400.0), 4),
+                    "socket_power_w_median": watts, "package_power_cap_w": _power_cap_w(),
+                    "note": "3 s back-to-back run; clock (rocm-smi) and socket power (amd-smi) "
+                            "sampled while it runs; peak scales with clock"}
+                log(f"  sustained {name}: {extra[f'sustained_clock_{name}']}")
 
     if args.copy_calibration:
-        src = torch.empty(128 << 20, dtype=torch.int16, device="cuda:0").fill_(1)
-        dst = torch.empty_like(src)
+        src_t = torch.empty(128 << 20, dtype=torch.int16, device="cuda:0").fill_(1)
+        dst_t = torch.empty_like(src_t)
         for _ in range(5):
-            dst.copy_(src)
+            dst_t.copy_(src_t)
         torch.cuda.synchronize()
         log("  copy calibration: 5 x 256 MiB read + 256 MiB written")
-        del src, dst
+        del src_t, dst_t
 
-    algo_bytes = 2 * (w.M * w.K + w.K * w.N) + (4 if w.out_dtype == W.F32 else 2) * w.M * w.N
     result = {
         "metric": METRIC,
-        "value": round(tflops, 2),
+        "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(kern_ms, 4),
-        "wall_ms_per_step": round(wall_ms, 4),
-        "wall_tflops": round(wall_tflops, 2),
+        "warmup_launches_run": t["warmup_launches_run"],
+        "warmup_s": t["warmup_s"],
+        "ms_per_step": round(t["mean_ms"], 4),
+        "kernel_us_median": head["kernel_us_median"],
+        "kernel_us_min": head["kernel_us_min"],
+        "wall_ms_per_step": round(t["wall_ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -516,17 +639,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in_dtype": w.in_dtype,
                    "out_dtype": w.out_dtype, "b_layout": w.b_layout, "epilogue": w.epilogue,
-                   "tile": cfg.as_dict(), "parallelism": "single GPU"},
+                   "inputs": list(w.dist), "tile": cfg.as_dict(), "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS[w.in_dtype], 2),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
-                     "peak": PEAK_TFLOPS[w.in_dtype], "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_TFLOPS[w.in_dtype], 4),
-                     "traffic": measured_traffic(w.name, cfg, w),
-                     "algorithmic_bytes": algo_bytes},
+        "roofline": head["roofline"],
         "extra": extra,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"] = cpu_baseline(w, 12.0)
     print(json.dumps(result), flush=True)
 
 

@@ -181,8 +181,19 @@ int32_t gemm_num_configs(void);
 gemm_status gemm_list_config(int32_t index, gemm_tile_config* out);
 
 /* LDS bytes a configuration needs: stages * (block_m + block_n) * block_k * 2, plus
- * block_m * block_k * 2 for staging 4. */
+ * block_m * block_k * 2 for staging 4 or block_n * block_k * 2 for staging 6.
+ * Returns -1 for a NULL cfg. */
 int64_t gemm_lds_bytes(const gemm_tile_config* cfg);
+
+/* Bounded waits of the wave-specialized ring (staging 3, the Pallas guide's
+ * warp-specialized pipeline with "consumed" counters) that gave up on the current
+ * device since the library was loaded or since the last reset.  Each wait on an LDS
+ * counter polls for about 0.1 s and then lets the wave go on instead of hanging; a
+ * give-up therefore means some launch produced a wrong C, and it is counted in a device
+ * word that this call reads back.  Waits for the device to finish all its work first;
+ * reset != 0 then clears the word.  *count receives the number (0 on error).
+ * Errors: INVALID_ARG (count NULL), HIP (no device, or a HIP call failed). */
+gemm_status gemm_wait_timeouts(uint32_t* count, int32_t reset);
 
 /* Human-readable name of a status code (static storage). */
 const char* gemm_status_string(gemm_status s);

@@ -72,7 +72,7 @@ class TileConfig(ctypes.Structure):
 
 EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_get_config", "gemm_autotune",
             "gemm_num_configs", "gemm_list_config", "gemm_lds_bytes", "gemm_status_string",
-            "gemm_last_hip_error", "gelu_run")
+            "gemm_last_hip_error", "gemm_wait_timeouts", "gelu_run")
 
 _lib = None
 
@@ -114,6 +114,8 @@ def lib():
     L.gemm_status_string.argtypes = [ctypes.c_int]
     L.gemm_last_hip_error.restype = ctypes.c_char_p
     L.gemm_last_hip_error.argtypes = []
+    L.gemm_wait_timeouts.restype = ctypes.c_int
+    L.gemm_wait_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32]
     L.gelu_run.restype = ctypes.c_int
     L.gelu_run.argtypes = [vp, vp, i64, ctypes.c_int, vp]
     _lib = L
@@ -201,6 +203,14 @@ def gemm_status_string(status: int) -> str:
 
 def gemm_last_hip_error() -> str:
     return lib().gemm_last_hip_error().decode()
+
+
+def gemm_wait_timeouts(reset: bool = False) -> int:
+    """Bounded waits of the wave-specialized ring that gave up on the current device
+    (synchronizes the device; reset clears the count after reading it)."""
+    n = ctypes.c_uint32()
+    _check(lib().gemm_wait_timeouts(ctypes.byref(n), 1 if reset else 0), "gemm_wait_timeouts")
+    return int(n.value)
 
 
 def gelu_run(x, y, n: int, dtype: str = "bf16", stream=None) -> None:

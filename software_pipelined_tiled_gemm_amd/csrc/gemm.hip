@@ -37,6 +37,11 @@ const char* last_hip_error() { return g_last_hip_error; }
 
 }  // namespace spg
 
+// Count of the wave-specialized ring's bounded waits that gave up (each device holds
+// its own copy of this word).  Kernels reach it through KArgs::wait_timeouts, the
+// address hipGetSymbolAddress gives for the launching device.
+static __device__ uint32_t g_wait_timeouts;
+
 using spg::hip_fail;
 using spg::KArgs;
 using spg::launch_fn;
@@ -155,8 +160,24 @@ int cu_count() {
     return n;
 }
 
+// Device address of g_wait_timeouts on the current device (resolved once per device;
+// nullptr if there is no device or the lookup fails).
+uint32_t* wait_word() {
+    static uint32_t* cache[64] = {nullptr};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    uint32_t* p = __atomic_load_n(&cache[dev], __ATOMIC_ACQUIRE);
+    if (p) return p;
+    if (hipGetSymbolAddress((void**)&p, HIP_SYMBOL(g_wait_timeouts)) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    __atomic_store_n(&cache[dev], p, __ATOMIC_RELEASE);
+    return p;
+}
+
 gemm_tile_config heuristic(int64_t M, int64_t N, gemm_b_layout bl) {
-    // Estimated time of a candidate = rounds of the 256 CUs it needs x its tile's
+    // Estimated time of a candidate = rounds of the device's CUs it needs x its tile's
     // area / its measured per-tile throughput relative to 256x256 (bf16 NN 8192^3
     // and the 1024x8192x8192 shard on MI355X: 256x128 runs at 0.91 of the 256x256
     // rate per output, 128x128 at 0.66, 192x256 at 0.80 (3072x4096x4096) to 0.88
@@ -167,7 +188,8 @@ gemm_tile_config heuristic(int64_t M, int64_t N, gemm_b_layout bl) {
     // The 8-wave tiles run 16x16x32 MFMAs (measured against 32x32x16 with the same
     // tile, interleaved in one process, +2..9% on every benchmark shape; fp16 and
     // [N,K] B gain the most), the 4-wave 128x128 tile 32x32x16.
-    const int64_t cus = 256;
+    const int cc = cu_count();
+    const int64_t cus = cc > 0 ? cc : 256;   // 256 on MI355X; also the planning default without a device
     struct Cand { int bm, bn, bk, st, wm, wn, mfma; double eff; };
     const Cand cands[] = {{256, 256, 64, 2, 128, 64, 16, 1.0},
                           {192, 256, 64, 2, 96, 64, 16, 0.85},
@@ -215,6 +237,7 @@ KArgs make_args(const gemm_plan* p, const void* A, const void* B, void* C, int b
     a.epilogue = (int32_t)p->epi;
     a.persistent = 0;
     a.store_direct = p->cfg.store ? 1 : 0;
+    a.wait_timeouts = wait_word();
     return a;
 }
 
@@ -278,6 +301,22 @@ const char* gemm_status_string(gemm_status s) {
 }
 
 const char* gemm_last_hip_error(void) { return spg::last_hip_error(); }
+
+gemm_status gemm_wait_timeouts(uint32_t* count, int32_t reset) {
+    if (!count) return GEMM_ERR_INVALID_ARG;
+    *count = 0;
+    uint32_t* p = wait_word();
+    if (!p) {
+        int n = 0;
+        const hipError_t e = hipGetDeviceCount(&n);
+        return hip_fail(e != hipSuccess ? e : hipErrorNoDevice);
+    }
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(count, p, sizeof(uint32_t), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && reset) e = hipMemset(p, 0, sizeof(uint32_t));
+    if (e == hipSuccess && reset) e = hipDeviceSynchronize();
+    return e == hipSuccess ? GEMM_OK : hip_fail(e);
+}
 
 int32_t gemm_num_configs(void) { return kNumVariants; }
 
@@ -355,6 +394,7 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
     p->simple = !pipelined_fits(M, N, K, b_layout);
     p->var = var;
     p->cfg = cfg;
+    (void)wait_word();   // resolve the device's error word now, outside any graph capture
     *out = p;
     return GEMM_OK;
 }

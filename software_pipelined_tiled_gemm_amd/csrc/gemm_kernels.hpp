@@ -87,6 +87,7 @@ struct KArgs {
     int32_t epilogue;
     int32_t persistent;   // launcher only: run the persistent instantiation (grid = CUs)
     int32_t store_direct; // 1: the epilogue stores from registers, without LDS staging
+    uint32_t* wait_timeouts;  // device word: bounded waits of the wave-specialized ring that gave up
 };
 
 // ---------------------------------------------------------------------------
@@ -1307,7 +1308,9 @@ pipelined_gemm(KArgs args) {
 // Consumers wait for full[t % S] >= t + 1 before reading k-tile t; the producer
 // waits for freed[s] >= NC * (t / S) before copying k-tile t into slot s.
 // Every wait is bounded (kSpinMax polls with s_sleep in between, ~0.1 s): if a
-// counter never arrived the wave goes on with wrong data instead of hanging.
+// counter never arrived the wave goes on with wrong data instead of hanging, and
+// adds 1 to the device word args.wait_timeouts, which the host reads back
+// (gemm_wait_timeouts), so a give-up is never silent.
 // The register file allots every wave of a workgroup the same VGPRs, so the
 // producer costs a consumer's worth of registers: with 128x64 consumer tiles
 // (two waves per SIMD at most) the tile is 256x128, four consumers + one producer.
@@ -1320,11 +1323,16 @@ constexpr int kSpinMax = 1 << 21;
 // before it adds to one.  The LDS executes one wave's operations in order, so
 // reads issued after a counter load has returned see what the counter announced;
 // the compiler fence keeps them after the loop.
-__device__ __forceinline__ void wait_at_least(uint32_t* p, uint32_t target) {
-    for (int it = 0; it < kSpinMax; ++it) {
+// A wait that exhausts its polls counts itself in *timeouts (one lane of the wave, a
+// device-scope atomic add: a vector memory instruction) and returns.
+__device__ __forceinline__ void wait_at_least(uint32_t* p, uint32_t target, uint32_t* timeouts) {
+    int it = 0;
+    for (; it < kSpinMax; ++it) {
         if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
         __builtin_amdgcn_s_sleep(2);
     }
+    if (it == kSpinMax && (threadIdx.x & 63) == 0 && timeouts != nullptr)
+        __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("" ::: "memory");
 }
 
@@ -1444,7 +1452,7 @@ ws_gemm(KArgs args) {
         };
         issue(0, true);
         for (int t = 1; t < nk; ++t) {
-            if (t >= S) wait_at_least(&freed[t % S], (uint32_t)(NC * (t / S)));
+            if (t >= S) wait_at_least(&freed[t % S], (uint32_t)(NC * (t / S)), args.wait_timeouts);
             issue(t, false);
             wait_vmcnt<L>();      // k-tile t-1 has landed
             publish(t - 1);
@@ -1508,7 +1516,7 @@ ws_gemm(KArgs args) {
             });
         };
         Frags f0, f1;
-        wait_at_least(&full[0], 1u);
+        wait_at_least(&full[0], 1u, args.wait_timeouts);
         static_for<0, NRD>([&](auto rc) { read_op(slot(0), 0, f0, rc); });
         for (int t = 0; t < nk; ++t) {
             const SPG_LDS char* cur = slot(t);
@@ -1520,7 +1528,7 @@ ws_gemm(KArgs args) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             if (lane == 0)
                 __hip_atomic_fetch_add(&freed[t % S], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (t + 1 < nk) wait_at_least(&full[(t + 1) % S], (uint32_t)(t + 2));
+            if (t + 1 < nk) wait_at_least(&full[(t + 1) % S], (uint32_t)(t + 2), args.wait_timeouts);
             // reads the first step of k-tile t+1 (a stale slot after the last one: unused)
             stage(f1, slot(t + 1), 0, f0);
         }
@@ -1558,15 +1566,18 @@ __global__ void __launch_bounds__(256) simple_gemm(KArgs a) {
     const int m0 = blockIdx.y * T, n0 = blockIdx.x * T;
     const int M = a.M, N = a.N, K = a.K;
     float acc[4][4] = {};
-    for (int k0 = 0; k0 < K; k0 += TK) {
+    // 64-bit k: K may be as large as INT32_MAX, where k0 + TK would overflow an int
+    for (int64_t k0 = 0; k0 < K; k0 += TK) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = tid + i * 256;
             const int r = e / TK, kk = e % TK;
-            const int gm = m0 + r, gk = k0 + kk;
+            const int gm = m0 + r;
+            const int64_t gk = k0 + kk;
             As[kk][r] = (gm < M && gk < K) ? bits_to_f32(a.A[(size_t)gm * K + gk], BF16) : 0.0f;
             const int kb = e / T, c = e % T;
-            const int gkb = k0 + kb, gn = n0 + c;
+            const int64_t gkb = k0 + kb;
+            const int gn = n0 + c;
             float bv = 0.0f;
             if (gkb < K && gn < N)
                 bv = bits_to_f32(B_NK ? a.B[(size_t)gn * K + gkb] : a.B[(size_t)gkb * N + gn], BF16);

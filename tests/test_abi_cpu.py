@@ -72,6 +72,24 @@ def test_invalid_arguments_rejected_without_gpu(L):
     assert L.gemm_get_config(None, None) == 1
     assert L.gemm_autotune(None, None, None, None, None, 1, None) == 1
     assert L.gemm_destroy(None) == 0
+    assert L.gemm_wait_timeouts(None, 0) == 1
+
+
+def test_wait_timeouts_without_a_device(L):
+    # the device word cannot be read without a GPU: a HIP error, and the count is zeroed
+    n = ctypes.c_uint32(7)
+    assert L.gemm_wait_timeouts(ctypes.byref(n), 0) == 4
+    assert n.value == 0
+
+
+def test_largest_k_plans_the_simple_kernel(L):
+    # K up to INT32_MAX is accepted (the simple kernel walks K with 64-bit indices); one
+    # more is unsupported
+    h = spg.gemm_create(8, 8, (1 << 31) - 1, "bf16", "f32", "nk")
+    assert spg.gemm_get_config(h).block_k == 0
+    spg.gemm_destroy(h)
+    hh = ctypes.c_void_p()
+    assert L.gemm_create(ctypes.byref(hh), 8, 8, 1 << 31, 1, 2, 1, 0, None) == 2
 
 
 def test_plan_lifecycle_and_pointer_checks(L):

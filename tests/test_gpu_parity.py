@@ -3,9 +3,9 @@
 Tolerance (the accepted reading of the bound): with s = sqrt(K) max|A| max|B|,
 fp32 output: max|C - C_ref| / s <= 1e-4; fp16/bf16 output: the error in excess
 of half an output ulp of C_ref, divided by s, <= 4e-3 (the literal err_lit is
-reported too).  Small and medium shapes compare every element; the full-size
-workloads compare whole sampled rows (all N columns of each) because the fp64
-oracle cannot do 10^12 flops in a test, plus properties of the whole C.
+reported too).  Every test compares every element of C with the oracle, the
+benchmark workloads at full size included (the oracle's OpenMP triple loop does
+8192^3 in about 15 s on 16 host cores).
 """
 
 import numpy as np
@@ -50,6 +50,8 @@ def test_all_variants_ragged(in_dtype, b_layout):
     for vals in results.values():
         for v in vals[1:]:
             assert np.array_equal(v, vals[0])
+    # the wave-specialized ring ran among them: none of its bounded waits gave up
+    assert spg.gemm_wait_timeouts(reset=True) == 0
 
 
 @pytest.mark.parametrize("out_dtype", [W.BF16, W.F32])
@@ -225,17 +227,15 @@ def test_largest_pipelined_operands(case):
     # whose columns past N must read as zero
     if case == "max_k_nk":
         w = W.custom(40, 40, (1 << 31) // 512 - 72, W.BF16, W.BF16, W.B_NK)   # K = 4,194,232
-        rows = None
     else:
         K = 16376
         N = ((1 << 31) // ((K + 64) * 2)) // 8 * 8                           # 65,312
         w = W.custom(48, N, K, W.BF16, W.BF16, W.B_KN)
-        rows = np.array([0, 17, 47])
     _log(f"{case}: {w.describe()}")
     a, b = W.make_inputs(w)
     C, cfg = G.run(w, a, b)
     assert cfg.block_k == 64, cfg
-    res = G.check(w, a, b, G.c_values(C, w, rows), rows=rows)
+    res = G.check(w, a, b, G.c_values(C, w))
     _log(f"  err_q={res['err_q']:.3e}")
 
 
@@ -272,9 +272,7 @@ def test_persistent_matches_oracle_and_twin(shape):
         C, used = G.run(w, a, b, force=pers)
         assert used.persistent == 1
         got = G.c_values(C, w)
-        big = M * N > 4_000_000
-        rows = np.unique(np.r_[0, 255, 256, M - 1, np.arange(0, M, 97)]) if big else None
-        G.check(w, a, b, got[rows] if big else got, rows=rows)
+        G.check(w, a, b, got)
         # the same tile, one workgroup per tile: the same k order, so the same bits
         C2, _ = G.run(w, a, b, force=twin)
         assert np.array_equal(G.c_values(C2, w), got)
@@ -359,38 +357,29 @@ def test_autotune_keeps_parity():
 FULL = ["tn_f16_256", "tn_f16_3000x5000x1000_f32out", "pallas_hopper_example",
         "nn_f16_2048x2048x1024_relu_f32out",
         "tn_f16_4096", "nn_bf16_3072x4096x4096_gelu", "nn_bf16_8192", "nn_f16_8192"]
-SAMPLE_ROWS = {"tn_f16_4096": 96, "nn_bf16_3072x4096x4096_gelu": 96, "nn_bf16_8192": 48,
-               "nn_f16_8192": 48}
 
 
 @pytest.mark.parametrize("name", FULL)
 def test_workload_full_size(name):
-    import torch
+    """Every benchmark workload in the configuration the benchmark times, every element of
+    C against the oracle."""
     w = W.WORKLOADS[name]
     _log(f"workload {name}: {w.describe()}")
     a, b = W.make_inputs(w)
     C, cfg = G.run(w, a, b)
     _log(f"  config {cfg}")
-    n = SAMPLE_ROWS.get(name)
-    if n is None:
-        G.check(w, a, b, G.c_values(C, w))
-        return
-    r = np.random.Generator(np.random.PCG64(77))
-    rows = np.sort(np.concatenate([[0, w.M - 1], r.choice(w.M, n - 2, replace=False)]))
-    res = G.check(w, a, b, G.c_values(C, w, rows), rows=rows)
-    _log(f"  sampled rows: err_lit={res['err_lit']:.3e} floor={res['floor']:.3e} "
+    got = G.c_values(C, w)
+    del C
+    res = G.check(w, a, b, got)
+    _log(f"  all {w.M * w.N} elements: err_lit={res['err_lit']:.3e} floor={res['floor']:.3e} "
          f"err_q={res['err_q']:.3e}")
-    # whole-C property: finite everywhere
-    Cf = C.float() if w.out_dtype == W.F32 else (
-        C.view(torch.bfloat16).float() if w.out_dtype == W.BF16 else C.view(torch.float16).float())
-    assert bool(torch.isfinite(Cf).all())
 
 
 @pytest.mark.parametrize("b_layout", [W.B_KN, W.B_NK])
 def test_full_size_fp32_output_isolates_the_accumulation(b_layout):
     """bf16 8192^3 (B stored [K,N] or [N,K]) in the tile configuration the benchmark times,
     with an fp32 output: nothing is rounded to 16 bits, so the literal bound (1e-4 for an
-    fp32 output) applies to the fp32 accumulation itself, on sampled rows against the
+    fp32 output) applies to the fp32 accumulation itself, on every element against the
     oracle."""
     w = W.custom(8192, 8192, 8192, W.BF16, W.F32, b_layout, "none", ("uniform", -1.0, 1.0),
                  name=f"{'nn' if b_layout == W.B_KN else 'tn'}_bf16_8192_f32out")
@@ -399,11 +388,54 @@ def test_full_size_fp32_output_isolates_the_accumulation(b_layout):
     C, cfg = G.run(w, a, b)
     _log(f"  config {cfg}")
     assert (cfg.block_m, cfg.block_n, cfg.mfma) == (256, 256, 16)
-    r = np.random.Generator(np.random.PCG64(78))
-    rows = np.sort(np.concatenate([[0, w.M - 1], r.choice(w.M, 30, replace=False)]))
-    res = G.check(w, a, b, G.c_values(C, w, rows), rows=rows)
-    _log(f"  sampled rows: err_lit={res['err_lit']:.3e} err_q={res['err_q']:.3e}")
+    got = G.c_values(C, w)
+    del C
+    res = G.check(w, a, b, got)
+    _log(f"  all elements: err_lit={res['err_lit']:.3e} err_q={res['err_q']:.3e}")
     assert res["err_lit"] <= 1e-4
+
+
+@pytest.mark.parametrize("in_dtype", [W.BF16, W.F16])
+def test_b_deep_ring_bitwise_at_full_size(in_dtype):
+    """The B-deep ring (staging 6), the default for B stored [K,N] on grids of several
+    rounds, at 8192^3 in the benchmark's configuration, against its two-slot twin (same
+    tile, MFMA shape and schedule, staging 0): the same k order, so C must be bitwise
+    equal over all 67M elements.  At this size copies land late and slots turn over 128
+    times per tile, which is where a slot refilled too early would show."""
+    import torch
+    w = W.custom(8192, 8192, 8192, in_dtype, in_dtype, W.B_KN, "none", ("uniform", -1.0, 1.0),
+                 name=f"nn_{in_dtype}_8192")
+    a, b = W.make_inputs(w)
+    with spg.Gemm(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.b_layout) as g:
+        deep = g.config()
+    assert deep.staging == 6, deep
+    twin = [c for c in _variants() if c.staging == 0 and (c.block_m, c.block_n, c.block_k,
+            c.stages, c.wave_m, c.wave_n, c.lookahead, c.schedule, c.mfma) ==
+            (deep.block_m, deep.block_n, deep.block_k, deep.stages, deep.wave_m, deep.wave_n,
+             deep.lookahead, deep.schedule, deep.mfma)][0]
+    twin.group_m, twin.xcd_remap = deep.group_m, deep.xcd_remap
+    _log(f"b-deep {deep} against {twin}: {w.describe()}")
+    C1, _ = G.run(w, a, b)
+    C2, used = G.run(w, a, b, force=twin)
+    assert used.staging == 0
+    assert torch.equal(C1, C2)
+
+
+def test_wave_specialized_ring_reports_no_timeouts():
+    """The wave-specialized ring (staging 3) on a ragged multi-tile shape: within
+    tolerance of the oracle, and none of its bounded waits gave up (the device word
+    that gemm_wait_timeouts reads stays 0)."""
+    ws = [c for c in _variants() if c.staging == 3]
+    assert ws
+    spg.gemm_wait_timeouts(reset=True)
+    for layout in (W.B_KN, W.B_NK):
+        w = W.custom(1000, 1096, 1000, W.F16, W.F16, layout, "gelu_tanh", ("uniform", -1.0, 1.0))
+        a, b = W.make_inputs(w)
+        _log(f"wave-specialized {ws[0]} {w.describe()}")
+        C, used = G.run(w, a, b, force=ws[0])
+        assert used.staging == 3
+        G.check(w, a, b, G.c_values(C, w))
+    assert spg.gemm_wait_timeouts(reset=True) == 0
 
 
 @pytest.mark.parametrize("shape", [(1000, 1100, 700), (3072, 4096, 4096)], ids=["ragged", "gelu_workload"])
@@ -411,7 +443,7 @@ def test_gemm_run_replays_in_a_hip_graph(shape):
     """gemm_run neither allocates nor synchronizes, so a caller can capture it in a HIP
     graph.  Captured once (torch.cuda.graph) and replayed several times, with eager work
     and synchronizations between the replays, every replay gives the eager result bitwise
-    (and the eager result is within tolerance of the oracle on sampled rows)."""
+    (and the eager result is within tolerance of the oracle on every element)."""
     import torch
     M, N, K = shape
     w = W.custom(M, N, K, W.BF16, W.BF16, W.B_KN, "gelu_tanh", ("uniform", -1.0, 1.0),
@@ -440,5 +472,4 @@ def test_gemm_run_replays_in_a_hip_graph(shape):
             torch.cuda.synchronize()
             assert torch.equal(C_graph, C_eager), f"replay {i}"
         del graph
-    rows = np.array([0, M // 3, M - 1])
-    G.check(w, a, b, G.c_values(C_eager, w, rows), rows=rows)
+    G.check(w, a, b, G.c_values(C_eager, w))

@@ -1,6 +1,8 @@
 """Seeded input generator: determinism, shapes, distributions, and its 16-bit rounding
 agrees with the oracle's independent encoder."""
 
+import os
+
 import numpy as np
 import pytest
 
@@ -48,3 +50,19 @@ def test_workload_table():
     assert t["tn_f16_3000x5000x1000_f32out"].out_dtype == W.F32
     assert t["nn_bf16_3072x4096x4096_gelu"].epilogue == "gelu_tanh"
     assert t["nn_f16_2048x2048x1024_relu_f32out"].epilogue == "relu"
+
+
+def test_pallas_example_shape_is_the_golden_one():
+    # the Pallas guide's Hopper matmul example shape (tests/golden/hopper_example_shape.txt)
+    golden = {}
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "hopper_example_shape.txt")
+    for line in open(path):
+        if line.strip() and not line.startswith("#"):
+            k, v = line.split()
+            golden[k] = int(v)
+    w = W.WORKLOADS["pallas_hopper_example"]
+    assert (w.M, w.N, w.K) == (golden["m"], golden["n"], golden["k"])
+    assert golden["m"] == 132 * golden["tile_m"] and golden["n"] == 4 * golden["tile_n"]
+    assert golden["k"] == 10 * golden["tile_k"]
+    assert w.in_dtype == W.F16 and w.b_layout == W.B_KN and w.dist == ("unit",)
