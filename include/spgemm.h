@@ -20,12 +20,19 @@
  *     B is [K,N] (GEMM_B_KN, leading dimension N) or [N,K] (GEMM_B_NK,
  *     leading dimension K).  C is [M,N] (leading dimension N).
  *   - A, B and C are device pointers owned by the caller; the library never
- *     frees or retains them.  C must not overlap A or B (not checked).  The
- *     pipelined kernel needs A, B and C 16-byte aligned; other pointers run the
- *     simple kernel.
+ *     frees or retains them.  C must not overlap A or B (not checked).  Any 2-byte
+ *     aligned pointer is accepted (4-byte for an fp32 C).  When the rows of A and B
+ *     are 16 bytes apart (K % 8 == 0, and N % 8 == 0 for B stored [K,N]) and A and
+ *     B are 16-byte aligned, k-tiles are copied straight from memory into LDS;
+ *     otherwise the same MFMA kernel stages them through registers with 16-byte
+ *     loads at any 2-byte alignment (copy mode 7 below).  A C that is not 16-byte
+ *     aligned is written with element stores.
  *   - Out-of-range elements of partial tiles contribute exactly zero and are
- *     never written: any M, N, K >= 0 is accepted.  M == 0 or N == 0 is a no-op;
- *     K == 0 writes epi(0) = 0 everywhere.
+ *     never written: any M, N, K >= 0 is accepted (the masked tails of the Triton
+ *     lecture notes' matmul, other = 0).  M == 0 or N == 0 is a no-op; K == 0
+ *     writes epi(0) = 0 everywhere.  K < 8, N < 8 with B stored [K,N], and
+ *     operands whose copy windows would exceed 2^31 bytes run a simple
+ *     bounds-checked kernel.
  *   - Errors are reported only through gemm_status; nothing aborts and no C++
  *     exception crosses this interface.  Argument checks run before any HIP
  *     call, so they behave the same on a machine without a GPU.
@@ -95,7 +102,15 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1, GEMM_EPI_RELU = 2 } ge
  *                       compiled with schedule = 1 (16x16x32 tiles);
  *                       5 = as 0, with a slot refilled one k-tile after its release
  *                       (the Pallas guide's release delay of 1; stages >= 3): S-1
- *                       k-tiles in flight instead of S
+ *                       k-tiles in flight instead of S;
+ *                       7 = as 1, for operands whose rows or base pointers are not
+ *                       16-byte aligned: 16-byte loads at any 2-byte alignment, the
+ *                       chunk that straddles k = 0 (first k-tile) or column N (B
+ *                       stored [K,N]) loaded from the 8-element window inside the
+ *                       valid range and shifted into place in registers, its
+ *                       out-of-range elements zeroed.  gemm_create plans it when
+ *                       K % 8 != 0 or (B stored [K,N]) N % 8 != 0, and gemm_run
+ *                       switches to it when A or B is not 16-byte aligned
  *   lookahead           MFMA k-steps between the LDS read of an operand fragment and
  *                       its use: 1 (two fragment sets in registers) or 2 (four sets;
  *                       block_k 64, stages >= 2)
@@ -164,9 +179,17 @@ gemm_status gemm_run(gemm_handle h, const void* A, const void* B, void* C, hipSt
 /* Release a plan.  NULL is a no-op. */
 gemm_status gemm_destroy(gemm_handle h);
 
-/* The configuration a plan will launch (a plan that falls back to the simple
- * kernel for unaligned operands reports block_k = 0). */
+/* The configuration a plan launches for 16-byte aligned A and B (copy mode 7 when
+ * the rows themselves are not 16 bytes apart); a plan on the simple kernel reports
+ * block_k = 0. */
 gemm_status gemm_get_config(gemm_handle h, gemm_tile_config* out);
+
+/* The configuration gemm_run would launch with these operand pointers: as
+ * gemm_get_config, except that an A or B that is not 16-byte aligned selects the
+ * plan's copy-mode-7 configuration.  No HIP call.  Errors: INVALID_ARG (NULL h or
+ * out). */
+gemm_status gemm_launch_config(gemm_handle h, const void* A, const void* B, const void* C,
+                               gemm_tile_config* out);
 
 /* Time every compiled configuration that fits the plan's problem on the caller's
  * buffers (C is overwritten), `reps` launches each after one warm-up, and make the

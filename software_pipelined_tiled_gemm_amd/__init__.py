@@ -26,7 +26,7 @@ DTYPES = {"f16": 0, "bf16": 1, "f32": 2}
 B_LAYOUTS = {"kn": 0, "nk": 1}
 EPILOGUES = {"none": 0, "gelu_tanh": 1, "relu": 2}
 STAGING = {0: "direct", 1: "vgpr", 2: "direct-spread", 3: "producer-wave", 4: "direct-a-deep",
-           5: "direct-late-release", 6: "direct-b-deep"}
+           5: "direct-late-release", 6: "direct-b-deep", 7: "vgpr-any-alignment"}
 
 
 class GemmError(RuntimeError):
@@ -70,7 +70,8 @@ class TileConfig(ctypes.Structure):
                 f"{', mfma 16x16x32' if d['mfma'] == 16 else ''})")
 
 
-EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_get_config", "gemm_autotune",
+EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_get_config", "gemm_launch_config",
+            "gemm_autotune",
             "gemm_num_configs", "gemm_list_config", "gemm_lds_bytes", "gemm_status_string",
             "gemm_last_hip_error", "gemm_wait_timeouts", "gelu_run")
 
@@ -102,6 +103,8 @@ def lib():
     L.gemm_destroy.argtypes = [vp]
     L.gemm_get_config.restype = ctypes.c_int
     L.gemm_get_config.argtypes = [vp, ctypes.POINTER(TileConfig)]
+    L.gemm_launch_config.restype = ctypes.c_int
+    L.gemm_launch_config.argtypes = [vp, vp, vp, vp, ctypes.POINTER(TileConfig)]
     L.gemm_autotune.restype = ctypes.c_int
     L.gemm_autotune.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
     L.gemm_num_configs.restype = i32
@@ -175,6 +178,14 @@ def gemm_get_config(handle: int) -> TileConfig:
     return c
 
 
+def gemm_launch_config(handle: int, A, B, C) -> TileConfig:
+    """The configuration gemm_run would launch with these operands (their alignment)."""
+    c = TileConfig()
+    _check(lib().gemm_launch_config(handle, _ptr(A), _ptr(B), _ptr(C), ctypes.byref(c)),
+           "gemm_launch_config")
+    return c
+
+
 def gemm_autotune(handle: int, A, B, C, stream=None, reps: int = 10) -> float:
     us = ctypes.c_double()
     st = lib().gemm_autotune(handle, _ptr(A), _ptr(B), _ptr(C), _stream(stream, A, B, C), reps,
@@ -235,6 +246,9 @@ class Gemm:
 
     def config(self) -> TileConfig:
         return gemm_get_config(self.handle)
+
+    def launch_config(self, A, B, C) -> TileConfig:
+        return gemm_launch_config(self.handle, A, B, C)
 
     def autotune(self, A, B, C, stream=None, reps=10) -> float:
         return gemm_autotune(self.handle, A, B, C, stream, reps)

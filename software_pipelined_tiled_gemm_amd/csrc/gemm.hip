@@ -108,9 +108,12 @@ struct gemm_plan {
     gemm_dtype in, out;
     gemm_b_layout bl;
     gemm_epilogue epi;
-    bool simple;       // operands do not meet the pipelined kernel's alignment rules
-    const Variant* var;
+    bool simple;        // a shape the pipelined kernel does not take (K == 0, K < 8, ...)
+    bool rows_aligned;  // every row of A and B starts 16 bytes after the previous one
+    const Variant* var;     // the configuration gemm_run launches for 16-byte aligned A and B
     gemm_tile_config cfg;
+    const Variant* uvar;    // its misaligned-operand twin (copy mode 7): A or B not 16-byte
+    gemm_tile_config ucfg;  // aligned at run time (the same as var when the rows are not)
 };
 
 namespace {
@@ -118,22 +121,31 @@ namespace {
 bool valid_dtype_in(int d) { return d == GEMM_F16 || d == GEMM_BF16; }
 bool valid_dtype_out(int d) { return d == GEMM_F16 || d == GEMM_BF16 || d == GEMM_F32; }
 
-// Shape conditions of the pipelined kernel: 16-B rows for the direct-to-LDS copies
-// and 32-bit buffer offsets.  A copy resource spans at most 256 rows of A (or of a
-// [N,K] B) or all of a [K,N] B, plus up to 63 k of the leading partial k-tile; it
-// must stay within 2^31 bytes so that the out-of-range offset 2^31 reads zero.
-// Anything else runs on the simple kernel.
+// Shape conditions of the pipelined kernel: 32-bit buffer offsets, and rows long
+// enough to hold one 8-element copy window.  A copy resource spans at most 256 rows of
+// A (or of a [N,K] B) or all of a [K,N] B, plus up to 63 k of the leading partial
+// k-tile; it must stay within 2^31 bytes so that the out-of-range offset 2^31 reads
+// zero.  A K-contiguous row (A, B stored [N,K]) must hold 8 elements (K >= 8), and so
+// must a row of B stored [K,N] (N >= 8): copy mode 7 loads a chunk that straddles the
+// edge of the valid range from the 8-element window inside the row.  Anything else
+// (K == 0 included, which writes epi(0)) runs on the simple kernel.
 bool pipelined_fits(int64_t M, int64_t N, int64_t K, gemm_b_layout bl) {
     if (K <= 0 || M <= 0 || N <= 0) return false;
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return false;
-    if (K % 8 != 0) return false;
+    if (K < 8) return false;
     const int64_t lim = (int64_t)1 << 31;
     if (256 * (K + 64) * 2 > lim) return false;
     if (bl == GEMM_B_KN) {
-        if (N % 8 != 0) return false;
+        if (N < 8) return false;
         if ((K + 64) * N * 2 > lim) return false;
     }
     return true;
+}
+
+// Rows of A and B 16 bytes apart: the direct-to-LDS copy modes need this (and 16-byte
+// aligned base pointers, checked at launch); otherwise copy mode 7 runs.
+bool rows_aligned(int64_t N, int64_t K, gemm_b_layout bl) {
+    return K % 8 == 0 && (bl == GEMM_B_NK || N % 8 == 0);
 }
 
 const Variant* find_cfg(int bm, int bn, int bk, int stages, int staging, int wm, int wn,
@@ -176,7 +188,7 @@ uint32_t* wait_word() {
     return p;
 }
 
-gemm_tile_config heuristic(int64_t M, int64_t N, gemm_b_layout bl) {
+gemm_tile_config heuristic(int64_t M, int64_t N, gemm_b_layout bl, bool aligned) {
     // Estimated time of a candidate = rounds of the device's CUs it needs x its tile's
     // area / its measured per-tile throughput relative to 256x256 (bf16 NN 8192^3
     // and the 1024x8192x8192 shard on MI355X: 256x128 runs at 0.91 of the 256x256
@@ -195,6 +207,25 @@ gemm_tile_config heuristic(int64_t M, int64_t N, gemm_b_layout bl) {
                           {192, 256, 64, 2, 96, 64, 16, 0.85},
                           {256, 128, 64, 3, 64, 64, 16, 0.91},
                           {128, 128, 64, 3, 64, 64, 32, 0.66}};
+    // Misaligned operands (copy mode 7, register-staged, 32x32x16): the same cost model
+    // over the tiles compiled for that mode
+    const Cand ucands[] = {{256, 256, 64, 2, 128, 64, 32, 1.0},
+                           {256, 128, 64, 3, 128, 64, 32, 0.85},
+                           {128, 128, 64, 3, 64, 64, 32, 0.66}};
+    if (!aligned) {
+        const Cand* ub = nullptr;
+        double ub_t = 0.0;
+        for (const Cand& c : ucands) {
+            const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+            const double t = (double)((tiles + cus - 1) / cus) * c.bm * c.bn / c.eff;
+            if (!ub || t < ub_t) { ub = &c; ub_t = t; }
+        }
+        gemm_tile_config c = find_cfg(ub->bm, ub->bn, ub->bk, ub->st, 7, ub->wm, ub->wn, 0, ub->mfma)->cfg;
+        c.group_m = kDefaultGroupM;
+        c.xcd_remap = 1;
+        return c;
+    }
+    (void)bl;
     const Cand* best = nullptr;
     double best_t = 0.0;
     for (const Cand& c : cands) {
@@ -221,6 +252,14 @@ gemm_tile_config heuristic(int64_t M, int64_t N, gemm_b_layout bl) {
     return c;
 }
 
+// Largest power of two (at most 16) dividing an address.
+int32_t alignment_of(const void* p) {
+    const uintptr_t v = (uintptr_t)p;
+    for (int32_t a = 16; a > 1; a >>= 1)
+        if (v % (uintptr_t)a == 0) return a;
+    return 1;
+}
+
 KArgs make_args(const gemm_plan* p, const void* A, const void* B, void* C, int bm, int bn) {
     KArgs a;
     a.A = (const uint16_t*)A;
@@ -238,6 +277,7 @@ KArgs make_args(const gemm_plan* p, const void* A, const void* B, void* C, int b
     a.persistent = 0;
     a.store_direct = p->cfg.store ? 1 : 0;
     a.wait_timeouts = wait_word();
+    a.c_align = alignment_of(C);
     return a;
 }
 
@@ -251,13 +291,31 @@ bool persistent_fits(const gemm_plan* p, const gemm_tile_config& c) {
     return true;
 }
 
-gemm_status launch_plan(const gemm_plan* p, const gemm_tile_config& cfg, const Variant* var,
+// The configuration a launch with these operand pointers runs: the simple kernel
+// (nullptr), `var`, or, when A or B is not 16-byte aligned and `var` copies straight
+// to LDS, the plan's misaligned-operand twin.  (C's alignment only selects 16-byte or
+// element stores inside the epilogue.)
+const Variant* pick(const gemm_plan* p, const gemm_tile_config& cfg, const Variant* var,
+                    const void* A, const void* B, gemm_tile_config* used) {
+    if (p->simple || var == nullptr) return nullptr;
+    const bool ab16 = ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0);
+    if (cfg.staging != 7 && !ab16) {
+        *used = p->ucfg;
+        used->group_m = cfg.group_m;
+        used->xcd_remap = cfg.xcd_remap;
+        return p->uvar;
+    }
+    *used = cfg;
+    return var;
+}
+
+gemm_status launch_plan(const gemm_plan* p, const gemm_tile_config& cfg_in, const Variant* var_in,
                         const void* A, const void* B, void* C, hipStream_t st) {
     const bool bf = p->in == GEMM_BF16;
     const bool nk = p->bl == GEMM_B_NK;
-    // 16-byte copies from A and B, 16-byte stores to C
-    const bool aligned = ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && ((uintptr_t)C % 16 == 0);
-    if (p->simple || !aligned || var == nullptr) {
+    gemm_tile_config cfg = cfg_in;
+    const Variant* var = pick(p, cfg_in, var_in, A, B, &cfg);
+    if (var == nullptr) {
         gemm_plan q = *p;
         q.cfg.group_m = 1;
         KArgs a = make_args(&q, A, B, C, 64, 64);
@@ -355,7 +413,7 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
             force->stages <= 0 || force->wave_m <= 0 || force->wave_n <= 0 ||
             force->group_m < 0 || (force->swizzle != 0 && force->swizzle != 1) ||
             (force->xcd_remap != 0 && force->xcd_remap != 1) ||
-            force->staging < 0 || force->staging > 6 ||
+            force->staging < 0 || force->staging > 7 ||
             (force->store != 0 && force->store != 1) ||
             (force->mfma != 0 && force->mfma != 16 && force->mfma != 32) ||
             (force->lookahead != 1 && force->lookahead != 2) ||
@@ -378,9 +436,19 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
                 have = true;
             }
         }
-        if (!have) cfg = heuristic(M, N, b_layout);
+        if (!have) cfg = heuristic(M, N, b_layout, rows_aligned(N, K, b_layout));
         var = find_variant(cfg);
         if (!var) return GEMM_ERR_INTERNAL;
+    }
+    // rows that are not 16 bytes apart only go through copy mode 7
+    const bool ra = rows_aligned(N, K, b_layout);
+    if (!ra && cfg.staging != 7 && pipelined_fits(M, N, K, b_layout)) return GEMM_ERR_UNSUPPORTED;
+    gemm_tile_config ucfg = cfg;
+    const Variant* uvar = var;
+    if (cfg.staging != 7) {
+        ucfg = heuristic(M, N, b_layout, false);
+        uvar = find_variant(ucfg);
+        if (!uvar) return GEMM_ERR_INTERNAL;
     }
     gemm_plan* p = new (std::nothrow) gemm_plan;
     if (!p) return GEMM_ERR_OUT_OF_MEMORY;
@@ -392,8 +460,11 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
     p->bl = b_layout;
     p->epi = epilogue;
     p->simple = !pipelined_fits(M, N, K, b_layout);
+    p->rows_aligned = ra;
     p->var = var;
     p->cfg = cfg;
+    p->uvar = uvar;
+    p->ucfg = ucfg;
     (void)wait_word();   // resolve the device's error word now, outside any graph capture
     *out = p;
     return GEMM_OK;
@@ -410,6 +481,17 @@ gemm_status gemm_get_config(gemm_handle h, gemm_tile_config* out) {
     if (h->simple) {
         *out = gemm_tile_config{64, 64, 0, 1, 64, 64, 0, 1, 0, 0};
     }
+    return GEMM_OK;
+}
+
+gemm_status gemm_launch_config(gemm_handle h, const void* A, const void* B, const void* C,
+                               gemm_tile_config* out) {
+    if (!h || !out) return GEMM_ERR_INVALID_ARG;
+    (void)C;
+    gemm_tile_config used = h->cfg;
+    if (pick(h, h->cfg, h->var, A, B, &used) == nullptr)
+        used = gemm_tile_config{64, 64, 0, 1, 64, 64, 0, 1, 0, 0};
+    *out = used;
     return GEMM_OK;
 }
 
@@ -443,8 +525,10 @@ gemm_status gemm_autotune(gemm_handle h, const void* A, const void* B, void* C,
     gemm_tile_config best_cfg = h->cfg;
     const Variant* best_var = h->var;
     const int groups[] = {4, 8, 16};
+    const bool need7 = !h->rows_aligned || (uintptr_t)A % 16 != 0 || (uintptr_t)B % 16 != 0;
     for (const Variant& v : kVariants) {
         if (v.cfg.swizzle == 0 || v.cfg.stages == 1) continue;  // ablations are not candidates
+        if (need7 && v.cfg.staging != 7) continue;              // direct copies need aligned rows
         for (int g : groups) {
             gemm_tile_config c = v.cfg;
             c.group_m = g;

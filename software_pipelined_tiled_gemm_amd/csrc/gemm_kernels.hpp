@@ -88,6 +88,7 @@ struct KArgs {
     int32_t persistent;   // launcher only: run the persistent instantiation (grid = CUs)
     int32_t store_direct; // 1: the epilogue stores from registers, without LDS staging
     uint32_t* wait_timeouts;  // device word: bounded waits of the wave-specialized ring that gave up
+    int32_t c_align;          // byte alignment of C's base address (1, 2, 4, 8 or 16)
 };
 
 // ---------------------------------------------------------------------------
@@ -123,6 +124,34 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, SPG_LDS char* lds_dst, 
                  :
                  : "s"(m0), "v"(voff), "s"(rsrc)
                  : "memory", "m0");
+}
+
+// The 8 16-bit elements of a 16-byte chunk as one little-endian 128-bit number (element
+// e in bits 16e .. 16e+15) shifted toward higher elements (shl) or lower ones (shr) by
+// `bits` (a multiple of 16, 0 .. 112, per lane); zeros come in.  Realigns the chunks the
+// misaligned-operand copy mode loads from a shifted window, and zeroes the elements of
+// the window that lie outside the operand's valid range in the same step.
+// Both are written as selects between values computed for either half, so that they
+// compile to v_cndmask rather than to branches around per-lane conditions.
+__device__ __forceinline__ u32x4 shl128(u32x4 v, uint32_t bits) {
+    const uint64_t lo = ((uint64_t)v.y << 32) | v.x, hi = ((uint64_t)v.w << 32) | v.z;
+    const uint32_t b = bits & 63u;              // shift within a 64-bit half
+    // lo >> (64 - b) for b in 1 .. 63, written so that every shift count is < 64
+    const uint64_t carry = b == 0 ? 0 : (lo >> 1) >> (63u - b);
+    const bool big = bits >= 64;
+    const uint64_t nhi = big ? lo << b : (hi << b) | carry;
+    const uint64_t nlo = big ? 0 : lo << b;
+    return u32x4{(uint32_t)nlo, (uint32_t)(nlo >> 32), (uint32_t)nhi, (uint32_t)(nhi >> 32)};
+}
+
+__device__ __forceinline__ u32x4 shr128(u32x4 v, uint32_t bits) {
+    const uint64_t lo = ((uint64_t)v.y << 32) | v.x, hi = ((uint64_t)v.w << 32) | v.z;
+    const uint32_t b = bits & 63u;
+    const uint64_t carry = b == 0 ? 0 : (hi << 1) << (63u - b);
+    const bool big = bits >= 64;
+    const uint64_t nlo = big ? hi >> b : (lo >> b) | carry;
+    const uint64_t nhi = big ? 0 : hi >> b;
+    return u32x4{(uint32_t)nlo, (uint32_t)(nlo >> 32), (uint32_t)nhi, (uint32_t)(nhi >> 32)};
 }
 
 // Wait until at most N vector-memory instructions of this wave are outstanding.
@@ -270,7 +299,8 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TN][TM], char* 
     static_assert(NP >= 1 && TM % NP == 0, "blocks per round must divide the wave's blocks");
     auto swz = [](int row) { return CPR >= 16 ? (row & 15) : ((row >> 1) & 7); };
     const int M = args.M, N = args.N;
-    const bool vec_ok = (N % E16) == 0;
+    // 16-byte stores need 16-byte rows and a 16-byte aligned C; otherwise element stores
+    const bool vec_ok = (N % E16) == 0 && args.c_align >= 16;
     const int lrow = lane & 31;
 #pragma unroll
     for (int g = 0; g < TM; g += NP) {
@@ -354,7 +384,7 @@ __device__ __forceinline__ void store_tile16(const floatx4 (&acc)[TN][TM], char*
     static_assert(TM % 2 == 0 && NB32 % NP == 0, "blocks per round must divide the wave's blocks");
     auto swz = [](int row) { return CPR >= 16 ? (row & 15) : ((row >> 1) & 7); };
     const int M = args.M, N = args.N;
-    const bool vec_ok = (N % E16) == 0;
+    const bool vec_ok = (N % E16) == 0 && args.c_align >= 16;
     const int lrow = lane & 15;
 #pragma unroll
     for (int g = 0; g < NB32; g += NP) {
@@ -426,7 +456,7 @@ __device__ __forceinline__ void store_direct16(const AccV (&acc)[TN][TM], const 
     const int M = args.M, N = args.N;
     const int ep = args.epilogue;
     const bool bf = args.out_dtype == kOutBF16;
-    const bool vec_ok = (N % 4) == 0;    // then every 4-output segment is 8-byte aligned
+    const bool vec_ok = (N % 4) == 0 && args.c_align >= 8;    // every 4-output segment 8-byte aligned
 #pragma unroll
     for (int bm = 0; bm < TM; ++bm) {
         __builtin_amdgcn_sched_barrier(0);
@@ -538,6 +568,17 @@ __device__ __forceinline__ int kswz_t(int r) {
 //      16x16x32 tiles it fits the registers only under the compiler's schedule
 //      (SCHED 1; the hand-placed one spills), and there it is the fastest measured
 //      configuration at bf16 8192^3 (NN -1.3% time against mode 0 hand-placed).
+//   7  register-staged as in 1, for operands whose rows or base addresses are not 16-byte
+//      aligned (K % 8 != 0, B stored [K,N] with N % 8 != 0, or a base pointer that is
+//      not 16-byte aligned): each lane loads its 16 bytes with a buffer_load_dwordx4 at
+//      any 2-byte alignment (ROCm runs compute queues in unaligned-access mode, which the
+//      gfx950 code generation assumes as well).  The partial k-tile may then start at any
+//      element: on k-tile 0 a chunk that straddles k = 0 is loaded from the window that
+//      starts at k = 0 and shifted up by the straddle (shl128), which also zeroes its k < 0
+//      elements.  For B stored [K,N], a chunk that straddles column N is loaded from the
+//      window that ends at column N (never past the end of B) and shifted down (shr128),
+//      zeroing its columns >= N.  Rows past M (A) or N (B stored [N,K]) read zero through
+//      the buffer resource as in the other modes.
 //   5  direct-to-LDS copies as in 0, but a slot is refilled one k-tile after its
 //      release (the release delay of 1 in the Pallas guide's terms): the window
 //      after barrier t copies k-tile t+S-1 into the slot released at barrier t-1, so
@@ -583,6 +624,7 @@ pipelined_gemm(KArgs args) {
     static_assert(LDM != 6 || (S == 2 && S * G::STAGE + G::B_BYTES <= 160 * 1024),
                   "B-deep ring: two slots plus one more B slot within the LDS");
     static_assert(LDM != 5 || S >= 3, "a late release needs a ring of three slots or more");
+    static_assert(LDM != 7 || (S >= 2 && !PERS), "misaligned operands: register staging, ring of >= 2 slots");
     static_assert(!PERS || S * G::STAGE + G::NW * 32 * WN * 2 <= 160 * 1024,
                   "persistent: ring + epilogue staging must fit the LDS");
     constexpr int TM = G::TM, TN = G::TN, A_BYTES = G::A_BYTES, KSTEPS = G::KSTEPS;
@@ -654,8 +696,11 @@ pipelined_gemm(KArgs args) {
     // the partial k-tile, when K % BK != 0, is the first one and its k < 0 part
     // reads as zeros.  Every later k-tile lies inside [0, K), so only the copies
     // of k-tile 0 (all issued before the K loop) carry per-lane masks.  pad is a
-    // multiple of 8 (K % 8 == 0), i.e. of the 16-byte copy granule.
+    // multiple of 8 (K % 8 == 0), i.e. of the 16-byte copy granule, except in copy
+    // mode 7, where the chunk that straddles k = 0 is realigned (see the mode list).
     const int pad = (BK - K % BK) % BK;
+    constexpr bool UNAL = LDM == 7;                 // misaligned-operand copy mode
+    constexpr bool REG = LDM == 1 || LDM == 7;      // k-tiles staged through VGPRs
 
     // ---- copy sources: one buffer resource per operand and k-tile -------------
     // The resource of k-tile kt starts at the tile's first k and ends where this
@@ -677,6 +722,14 @@ pipelined_gemm(KArgs args) {
         b_base = (uint64_t)(uintptr_t)(args.B + n0);
         b_bytes = (uint32_t)(((size_t)K * N - n0) * 2u);
         b_kb = 2u * (uint32_t)N;
+        if constexpr (UNAL) {
+            // in mode 7 the window of a chunk that straddles N starts up to 7 columns
+            // before n0 when the last column tile holds fewer than 8 columns: the resource
+            // starts 16 bytes earlier so that every window offset is non-negative (an
+            // offset is an unsigned 32-bit value; a negative one would read zero)
+            b_base -= 16u;
+            b_bytes += 16u;
+        }
     }
     // start address and size of an operand's resource for k-tile kt
     auto window = [&](uint64_t base, uint32_t bytes, uint32_t kb, int kt, uint64_t& p,
@@ -707,7 +760,9 @@ pipelined_gemm(KArgs args) {
     // lands at byte i*16, i.e. row d*RPI + i/CPR, physical chunk i%CPR; it fetches
     // the logical chunk that the swizzle puts there.  kinA/kinB: the k offset of the
     // lane's 8 elements inside the k-tile, for the masks of k-tile 0.  Columns past
-    // N of a [K,N] B point past every resource and read as zero.
+    // N of a [K,N] B point past every resource and read as zero; in mode 7 a chunk that
+    // straddles N is loaded from the window ending at N and shifted down by the number
+    // of its columns past N, kept in 3 bits per op of nsh_pack (one register).
     uint32_t offA[A_DMA];
     int kinA[A_DMA];
 #pragma unroll
@@ -721,6 +776,8 @@ pipelined_gemm(KArgs args) {
     }
     uint32_t offB[B_DMA];
     int kinB[B_DMA];
+    uint32_t nsh_pack = 0;
+    static_assert(3 * B_DMA <= 32, "column shifts packed 3 bits per op");
 #pragma unroll
     for (int j = 0; j < B_DMA; ++j) {
         const int d = wave * B_DMA + j;
@@ -736,24 +793,43 @@ pipelined_gemm(KArgs args) {
             const int r = d * RP + lane / CPR;
             const int p = lane % CPR;
             const int c = SWZ ? (p ^ nswz(r)) : p;
-            offB[j] = n0 + c * 8 + 8 > N ? kOOB : (uint32_t)r * (uint32_t)N * 2u + (uint32_t)c * 16u;
+            const int over = n0 + c * 8 + 8 - N;    // columns of the chunk at or past N
+            if constexpr (UNAL) {
+                offB[j] = over >= 8 ? kOOB
+                                    : 16u + (uint32_t)r * (uint32_t)N * 2u + (uint32_t)c * 16u
+                                          - (over > 0 ? 2u * (uint32_t)over : 0u);
+                nsh_pack |= (over > 0 && over < 8 ? (uint32_t)over : 0u) << (3 * j);
+            } else {
+                offB[j] = over > 0 ? kOOB : (uint32_t)r * (uint32_t)N * 2u + (uint32_t)c * 16u;
+            }
             kinB[j] = r;
         }
     }
 
     // Offset of copy op j (compile-time): j < A_DMA moves A rows, the rest B.  On
-    // k-tile 0 (FIRST) the lanes whose elements lie at k < 0 read zero.
+    // k-tile 0 (FIRST) the lanes whose elements lie at k < 0 read zero; in mode 7 a
+    // K-contiguous chunk with only some elements at k < 0 reads the window that starts
+    // at k = 0 (kin + 8 > pad > kin), realigned by k0_shift before its LDS write.
+    auto first_off = [&](uint32_t off, int kin, bool k_contiguous) __attribute__((always_inline)) -> uint32_t {
+        if (kin >= pad) return off;
+        if (!UNAL || !k_contiguous || kin + 8 <= pad) return kOOB;
+        return off + 2u * (uint32_t)(pad - kin);
+    };
     auto src_off = [&](auto jc, auto first) __attribute__((always_inline)) -> uint32_t {
         constexpr int j = decltype(jc)::value;
         constexpr bool FIRST = decltype(first)::value;
         if constexpr (j < A_DMA) {
-            if constexpr (FIRST) return kinA[j] < pad ? kOOB : offA[j];
+            if constexpr (FIRST) return first_off(offA[j], kinA[j], true);
             else return offA[j];
         } else {
             constexpr int jb = j - A_DMA;
-            if constexpr (FIRST) return kinB[jb] < pad ? kOOB : offB[jb];
+            if constexpr (FIRST) return first_off(offB[jb], kinB[jb], B_NK);
             else return offB[jb];
         }
+    };
+    // mode 7, k-tile 0: bits to shift a K-contiguous chunk that straddles k = 0 up by
+    auto k0_shift = [&](int kin) __attribute__((always_inline)) -> uint32_t {
+        return kin < pad && kin + 8 > pad ? 16u * (uint32_t)(pad - kin) : 0u;
     };
     // op j writes LDS bytes lds_off(j) + 16*lane of the slot's A part (j < A_DMA) or
     // B part
@@ -772,16 +848,28 @@ pipelined_gemm(KArgs args) {
         constexpr int j = decltype(jc)::value;
         dma16(j < A_DMA ? src.a : src.b, part(slot, jc) + lds_off(jc), src_off(jc, first));
     };
-    // register staging (LDM 1): one k-tile of copies in flight in VGPRs
+    // register staging (LDM 1 and 7): one k-tile of copies in flight in VGPRs
     u32x4 stage_regs[G::L];
     auto gload_op = [&](const RegSrc& src, auto jc, auto first) __attribute__((always_inline)) {
         constexpr int j = decltype(jc)::value;
         stage_regs[j] = __builtin_amdgcn_raw_buffer_load_b128(j < A_DMA ? src.a : src.b,
                                                               (int)src_off(jc, first), 0, 0);
     };
-    auto lwrite_op = [&](const Slot& slot, auto jc) __attribute__((always_inline)) {
+    // write op j of the staged k-tile (FIRST: k-tile 0) into its slot; mode 7 realigns it
+    auto lwrite_op = [&](const Slot& slot, auto jc, auto first) __attribute__((always_inline)) {
         constexpr int j = decltype(jc)::value;
-        *(SPG_LDS u32x4*)(part(slot, jc) + lds_off(jc) + lane * 16) = stage_regs[j];
+        constexpr bool FIRST = decltype(first)::value;
+        u32x4 v = stage_regs[j];
+        if constexpr (UNAL) {
+            if constexpr (j < A_DMA) {
+                if constexpr (FIRST) v = shl128(v, k0_shift(kinA[j]));
+            } else if constexpr (B_NK) {
+                if constexpr (FIRST) v = shl128(v, k0_shift(kinB[j - A_DMA]));
+            } else {
+                v = shr128(v, 16u * ((nsh_pack >> (3 * (j - A_DMA))) & 7u));
+            }
+        }
+        *(SPG_LDS u32x4*)(part(slot, jc) + lds_off(jc) + lane * 16) = v;
     };
     auto issue = [&](const Slot& slot, int kt, auto first) __attribute__((always_inline)) {
         const DmaSrc src = dma_src(kt);
@@ -992,7 +1080,7 @@ pipelined_gemm(KArgs args) {
                 dma_op(cslot, src, std::integral_constant<int, j>{}, NotFirst{});
             }
             if constexpr (MD == 2 && i < NCP) {
-                lwrite_op(cslot, std::integral_constant<int, J0 + i>{});
+                lwrite_op(cslot, std::integral_constant<int, J0 + i>{}, NotFirst{});
                 gload_op(src, std::integral_constant<int, J0 + i>{}, NotFirst{});
             }
             if constexpr (MD == 3 && i < NCP)
@@ -1038,7 +1126,7 @@ pipelined_gemm(KArgs args) {
     Frags fr[NF];
     auto fset = [&](auto ic) -> Frags& { return fr[decltype(ic)::value % NF]; };
     constexpr bool DIRECT = LDM == 0 || LDM == 4 || LDM == 5 || LDM == 6;  // all copies of a window right after its barrier
-    using ModeWin = std::integral_constant<int, DIRECT ? 1 : (LDM == 1 ? 2 : 3)>;
+    using ModeWin = std::integral_constant<int, DIRECT ? 1 : (REG ? 2 : 3)>;
     constexpr int WOPS = DIRECT ? G::L / PF : CPS;    // copy ops per window stage
     static_assert(!DIRECT || G::L % PF == 0, "copies must split over the lookahead stages");
 
@@ -1129,12 +1217,12 @@ pipelined_gemm(KArgs args) {
             static_for<0, S - 1>([&](auto sc) {
                 const RegSrc src = reg_src(sc.value);
                 static_for<0, G::L>([&](auto jc) { gload_op(src, jc, first_of(sc)); });
-                static_for<0, G::L>([&](auto jc) { lwrite_op(slot_of(sc), jc); });
+                static_for<0, G::L>([&](auto jc) { lwrite_op(slot_of(sc), jc, first_of(sc)); });
             });
             const RegSrc src1 = reg_src(S - 1), src2 = reg_src(S);
             static_for<0, G::L>([&](auto jc) { gload_op(src1, jc, NotFirst{}); });
             static_for<0, PRE>([&](auto jc) {
-                lwrite_op(slot_of(std::integral_constant<int, S - 1>{}), jc);
+                lwrite_op(slot_of(std::integral_constant<int, S - 1>{}), jc, NotFirst{});
                 gload_op(src2, jc, NotFirst{});
             });
         }
@@ -1156,7 +1244,7 @@ pipelined_gemm(KArgs args) {
             const Slot prev = slot_at(std::integral_constant<int, (s + NS - 1) % NS>{});
             const Slot nxt = slot_at(std::integral_constant<int, (s + 1) % NS>{});
             auto src_of = [&](int kt) __attribute__((always_inline)) {
-                if constexpr (LDM == 1) return reg_src(kt);
+                if constexpr (REG) return reg_src(kt);
                 else return dma_src(kt);
             };
             if constexpr (DIRECT) {
@@ -1167,14 +1255,14 @@ pipelined_gemm(KArgs args) {
             } else {
                 // the window that started at barrier t-1: k-tile t+S-1 into prev
                 // (register staging: write k-tile t+S-1, load k-tile t+S)
-                const auto src = src_of(LDM == 1 ? t + S : t + S - 1);
+                const auto src = src_of(REG ? t + S : t + S - 1);
                 static_for<0, KSTEPS - PF>([&](auto kc) {
                     constexpr int kk = decltype(kc)::value;
                     using Pos = std::integral_constant<int, PF + kk>;
                     kstage(kc, cur, nxt, prev, src, Pos{}, T_{});
                 });
             }
-            if constexpr (LDM != 1) wait_vmcnt<STEADY>();
+            if constexpr (!REG) wait_vmcnt<STEADY>();
             // every wave has finished reading slot s (released) and the next k-tile is
             // complete in its slot
             lds_barrier();
@@ -1193,7 +1281,7 @@ pipelined_gemm(KArgs args) {
                     else if constexpr (LDM == 4) return DmaSrc{dma_src(t + 3).a, dma_src(t + 2).b};
                     else if constexpr (LDM == 6) return DmaSrc{dma_src(t + 2).a, dma_src(t + 3).b};
                     else if constexpr (LDM == 5) return dma_src(t + S - 1);
-                    else return src_of(LDM == 1 ? t + S + 1 : t + S);
+                    else return src_of(REG ? t + S + 1 : t + S);
                 }();
                 // the slot refilled: the one released here, or (release delay 1) the one
                 // released at the previous barrier

@@ -165,7 +165,7 @@ def test_forced_configs(L):
             assert c.stages == 2 and spg.gemm_lds_bytes(c) <= 160 * 1024
     assert deep == {4, 6}
     bad_staging = spg.TileConfig(block_m=256, block_n=256, block_k=64, stages=2, wave_m=128,
-                                 wave_n=64, swizzle=1, group_m=4, xcd_remap=1, staging=7)
+                                 wave_n=64, swizzle=1, group_m=4, xcd_remap=1, staging=8)
     with pytest.raises(spg.GemmError) as e:
         spg.gemm_create(512, 512, 512, force=bad_staging)
     assert e.value.status == 1
@@ -189,17 +189,53 @@ def test_lds_budget_is_the_tilelang_formula(L):
         assert spg.gemm_lds_bytes(c) == want
 
 
-def test_unaligned_shapes_plan_the_simple_kernel(L):
-    # K % 8 != 0 cannot feed 16-byte direct-to-LDS copies: the plan reports block_k = 0
-    h = spg.gemm_create(100, 100, 77, "f16", "f16", "nk")
-    assert spg.gemm_get_config(h).block_k == 0
-    spg.gemm_destroy(h)
-    h = spg.gemm_create(100, 101, 64, "bf16", "bf16", "kn")   # [K,N] rows not 16-B
-    assert spg.gemm_get_config(h).block_k == 0
-    spg.gemm_destroy(h)
+def test_misaligned_rows_plan_the_register_staged_mfma_path(L):
+    # K % 8 != 0 (or B stored [K,N] with N % 8 != 0): rows are not 16 bytes apart, so the
+    # plan is copy mode 7 (register-staged loads at any 2-byte alignment), block_k 64
+    for (M, N, K, layout) in ((100, 100, 77, "nk"), (100, 101, 64, "kn"), (3000, 5000, 1001, "nk"),
+                              (100, 100, 9, "kn"), (8, 8, 8, "kn")):
+        h = spg.gemm_create(M, N, K, "f16", "f16", layout)
+        c = spg.gemm_get_config(h)
+        spg.gemm_destroy(h)
+        aligned = K % 8 == 0 and (layout == "nk" or N % 8 == 0)
+        assert c.block_k == 64 and (c.staging == 7) != aligned, (M, N, K, layout, c)
+        assert c.mfma == 32
     h = spg.gemm_create(100, 101, 64, "bf16", "bf16", "nk")   # [N,K] rows are 16-B
+    assert spg.gemm_get_config(h).block_k == 64 and spg.gemm_get_config(h).staging != 7
+    spg.gemm_destroy(h)
+    # K < 8, or N < 8 with B stored [K,N]: no 8-element window fits a row: simple kernel
+    for (M, N, K, layout) in ((100, 100, 7, "nk"), (100, 5, 64, "kn"), (3, 3, 1, "kn")):
+        h = spg.gemm_create(M, N, K, "f16", "f16", layout)
+        assert spg.gemm_get_config(h).block_k == 0, (M, N, K, layout)
+        spg.gemm_destroy(h)
+    h = spg.gemm_create(100, 5, 64, "f16", "f16", "nk")       # a [N,K] B may have N < 8
     assert spg.gemm_get_config(h).block_k == 64
     spg.gemm_destroy(h)
+
+
+def test_misaligned_pointers_select_the_twin(L):
+    # the launch configuration follows the alignment of A and B (host logic, no launch):
+    # 16-byte aligned -> the plan's direct-copy configuration; otherwise its mode-7 twin
+    h = spg.gemm_create(4096, 4096, 4096, "bf16", "bf16", "kn")
+    base = spg.gemm_get_config(h)
+    assert base.staging != 7
+    assert spg.gemm_launch_config(h, 1 << 20, 2 << 20, 3 << 20).as_dict() == base.as_dict()
+    for a, b in ((2 + (1 << 20), 2 << 20), (1 << 20, 8 + (2 << 20))):
+        u = spg.gemm_launch_config(h, a, b, 3 << 20)
+        assert u.staging == 7 and u.block_k == 64 and u.group_m == base.group_m
+    # C's alignment does not change the configuration (element stores in the epilogue)
+    assert spg.gemm_launch_config(h, 1 << 20, 2 << 20, 2 + (3 << 20)).staging == base.staging
+    spg.gemm_destroy(h)
+    # a plan on the simple kernel reports block_k = 0 whatever the pointers
+    h = spg.gemm_create(10, 10, 3, "bf16", "bf16", "kn")
+    assert spg.gemm_launch_config(h, 1 << 20, 2 << 20, 3 << 20).block_k == 0
+    spg.gemm_destroy(h)
+    # forcing a direct-copy configuration onto rows that are not 16 bytes apart is refused
+    c = [spg.gemm_list_config(i) for i in range(spg.gemm_num_configs())]
+    direct = [x for x in c if x.staging == 0][0]
+    with pytest.raises(spg.GemmError) as e:
+        spg.gemm_create(512, 512, 500, force=direct)
+    assert e.value.status == 2
 
 
 def test_size_limits_of_the_pipelined_kernel(L):

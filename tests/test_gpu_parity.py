@@ -86,7 +86,8 @@ def test_output_dtypes_and_epilogue(out_dtype, epilogue):
 
 
 # ---------------------------------------------------------------------------
-# small shapes: masks on M, N and K, and the simple kernel for unaligned K / N
+# small shapes: masks on M, N and K; rows that are not 16 bytes apart run the
+# register-staged copy mode 7 of the same MFMA kernel
 # ---------------------------------------------------------------------------
 
 SIZES = [1, 2, 3, 7, 8, 15, 16, 17, 31, 33, 63, 64, 65, 127, 129]
@@ -113,6 +114,12 @@ def test_small_shapes(b_layout, in_dtype):
             w = W.custom(M, N, K, in_dtype, out_dtype, b_layout, epi)
             a, b = W.make_inputs(w)
             C, cfg = G.run(w, a, b)
+            # every shape whose rows hold an 8-element copy window runs the MFMA kernel
+            mfma_path = K >= 8 and (b_layout == W.B_NK or N >= 8)
+            assert (cfg.block_k == 64) == mfma_path, (M, N, K, cfg)
+            aligned_rows = K % 8 == 0 and (b_layout == W.B_NK or N % 8 == 0)
+            if mfma_path:
+                assert (cfg.staging == 7) != aligned_rows, (M, N, K, cfg)
             G.check(w, a, b, G.c_values(C, w))
 
 
@@ -132,16 +139,30 @@ def test_empty_and_k_zero():
         assert torch.all(C == 0)
 
 
-def test_misaligned_pointers_take_the_simple_path():
+def _offset_copy(bits, elems):
+    """A device copy of bits that starts `elems` 2-byte elements into its buffer."""
     import torch
-    w = W.custom(100, 72, 64, W.F16, W.F16, W.B_NK)
+    buf = torch.zeros(bits.size + elems + 8, dtype=torch.int16, device=G.torch_dev())
+    buf[elems:elems + bits.size] = G.to_dev(bits).reshape(-1)
+    return buf, buf[elems:elems + bits.size]
+
+
+@pytest.mark.parametrize("b_layout", [W.B_KN, W.B_NK])
+@pytest.mark.parametrize("which", ["A", "B", "AB"])
+def test_misaligned_pointers_run_the_mfma_path(b_layout, which):
+    """A or B starting 2 (or 6) bytes past a 16-byte boundary: gemm_run switches to the
+    plan's copy-mode-7 twin (16-byte loads at any 2-byte alignment), same MFMA kernel."""
+    import torch
+    w = W.custom(300, 520, 200, W.F16, W.F16, b_layout, "gelu_tanh", ("uniform", -1.0, 1.0))
     a, b = W.make_inputs(w)
-    A = torch.zeros(a.size + 1, dtype=torch.int16, device=G.torch_dev())
-    A[1:] = G.to_dev(a).reshape(-1)
-    B = G.to_dev(b)
+    _, A = _offset_copy(a, 1 if "A" in which else 0)
+    _, B = _offset_copy(b, 3 if "B" in which else 0)
     C = G.alloc_c(w)
-    with spg.Gemm(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.b_layout) as g:
-        g(A[1:].data_ptr(), B, C)     # A is only 2-byte aligned
+    with spg.Gemm(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.b_layout, w.epilogue) as g:
+        used = g.launch_config(A.data_ptr(), B.data_ptr(), C.data_ptr())
+        assert used.staging == 7 and used.block_k == 64, used
+        assert g.config().staging != 7
+        g(A.data_ptr(), B.data_ptr(), C)
     torch.cuda.synchronize()
     G.check(w, a, b, G.c_values(C, w))
 
@@ -165,17 +186,26 @@ def test_mfma16_gelu_and_direct_store(out_dtype):
             assert np.array_equal(G.c_values(C2, w), got)
 
 
-def test_misaligned_output_takes_the_simple_path():
+@pytest.mark.parametrize("out_dtype", [W.BF16, W.F32])
+def test_misaligned_output_keeps_the_configuration(out_dtype):
+    """C starting 2 (bf16) or 4 (fp32) bytes past a 16-byte boundary: the same
+    configuration runs, its epilogue writes elements instead of 16-byte vectors, and
+    nothing outside C is touched."""
     import torch
-    w = W.custom(100, 72, 64, W.BF16, W.BF16, W.B_KN)
+    w = W.custom(100, 72, 64, W.BF16, out_dtype, W.B_KN)
     a, b = W.make_inputs(w)
     A, B = G.to_dev(a), G.to_dev(b)
-    big = torch.zeros(w.M * w.N + 1, dtype=torch.int16, device=G.torch_dev())
-    C = big[1:].view(w.M, w.N)                     # 2-byte aligned
+    if out_dtype == W.F32:
+        big = torch.zeros(w.M * w.N + 2, dtype=torch.float32, device=G.torch_dev())
+    else:
+        big = torch.zeros(w.M * w.N + 2, dtype=torch.int16, device=G.torch_dev())
+    C = big[1:1 + w.M * w.N].view(w.M, w.N)
     with spg.Gemm(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.b_layout) as g:
+        assert g.launch_config(A, B, C).as_dict() == g.config().as_dict()
+        assert g.config().block_k == 64
         g(A, B, C)
     torch.cuda.synchronize()
-    assert int(big[0]) == 0
+    assert float(big[0]) == 0 and float(big[-1]) == 0
     G.check(w, a, b, G.c_values(C, w))
 
 
@@ -339,6 +369,77 @@ def test_b_deep_ring_epilogues_and_outputs():
         G.check(w, a, b, got)
         C2, _ = G.run(w, a, b, force=twin)
         assert np.array_equal(G.c_values(C2, w), got)
+
+
+def _mode7():
+    return [c for c in _variants() if c.staging == 7]
+
+
+# K residues mod 8 and mod 64, K just above 8 and one partial k-tile; N with residues
+# mod 8 (B stored [K,N]); M and N ragged against every tile; last column tiles with
+# fewer than 8 columns (263 = 2 x 128 + 7, 517 = 2 x 256 + 5), whose straddling chunk
+# is loaded from a window that starts before the tile
+MISALIGNED = [(300, 520, 9), (257, 264, 63), (130, 300, 65), (520, 648, 1001), (64, 136, 15),
+              (300, 131, 200), (33, 257, 127), (600, 523, 760), (96, 9, 64), (129, 129, 129),
+              (300, 263, 200), (300, 517, 100)]
+
+
+@pytest.mark.parametrize("b_layout", [W.B_KN, W.B_NK])
+def test_misaligned_rows_every_mode7_configuration(b_layout):
+    """Rows that are not 16 bytes apart, through every compiled copy-mode-7
+    configuration, fp16 and bf16, every output type and epilogue, against the oracle."""
+    cfgs = _mode7()
+    assert len(cfgs) >= 3
+    for i, (M, N, K) in enumerate(MISALIGNED):
+        in_dtype = (W.F16, W.BF16)[i % 2]
+        out_dtype = (W.F16, W.BF16, W.F32)[i % 3]
+        epi = ("none", "gelu_tanh", "relu")[i % 3]
+        w = W.custom(M, N, K, in_dtype, out_dtype, b_layout, epi, ("uniform", -1.0, 1.0))
+        a, b = W.make_inputs(w)
+        for c in cfgs:
+            _log(f"mode 7 {c} {w.describe()}")
+            C, used = G.run(w, a, b, force=c)
+            assert used.staging == 7
+            G.check(w, a, b, G.c_values(C, w))
+
+
+def test_mode7_bitwise_equals_its_register_staged_twin():
+    """On 16-byte aligned operands copy mode 7 computes exactly what copy mode 1 (the same
+    register staging without realignment) does with the same tile: the same k order, so
+    the same bits, with and without a partial k-tile, both layouts."""
+    for c in _mode7():
+        twin = [t for t in _variants() if t.staging == 1 and (t.block_m, t.block_n, t.block_k,
+                t.stages, t.wave_m, t.wave_n, t.mfma, t.schedule, t.lookahead) ==
+                (c.block_m, c.block_n, c.block_k, c.stages, c.wave_m, c.wave_n, c.mfma,
+                 c.schedule, c.lookahead)]
+        assert twin, f"no register-staged twin of {c}"
+        for layout in (W.B_KN, W.B_NK):
+            for K in (200, 512):
+                w = W.custom(520, 648, K, W.BF16, W.BF16, layout, "none", ("uniform", -1.0, 1.0))
+                a, b = W.make_inputs(w)
+                C1, _ = G.run(w, a, b, force=c)
+                C2, _ = G.run(w, a, b, force=twin[0])
+                assert np.array_equal(G.c_values(C1, w), G.c_values(C2, w)), (c, layout, K)
+
+
+@pytest.mark.parametrize("shape", [(3000, 5000, 1001, W.F16, W.F32, W.B_NK),
+                                   (3000, 3001, 1000, W.BF16, W.BF16, W.B_KN),
+                                   (4096, 4096, 4095, W.F16, W.F16, W.B_NK)],
+                         ids=["K1001_tn", "N3001_nn", "K4095_tn"])
+def test_misaligned_rows_full_size(shape):
+    """The K % 8 != 0 neighbour of the masked-tail workload, a [K,N] B with N % 8 != 0,
+    and a 4096^2 problem with K = 4095, in the configuration the library picks, every
+    element against the oracle."""
+    M, N, K, dt, od, layout = shape
+    w = W.custom(M, N, K, dt, od, layout, "none", ("uniform", -1.0, 1.0))
+    _log(f"full size misaligned rows: {w.describe()}")
+    a, b = W.make_inputs(w)
+    C, cfg = G.run(w, a, b)
+    assert cfg.staging == 7 and cfg.block_k == 64, cfg
+    got = G.c_values(C, w)
+    del C
+    res = G.check(w, a, b, got)
+    _log(f"  err_lit={res['err_lit']:.3e} err_q={res['err_q']:.3e}")
 
 
 def test_autotune_keeps_parity():
