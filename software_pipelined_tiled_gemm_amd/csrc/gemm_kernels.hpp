@@ -278,10 +278,16 @@ __device__ __forceinline__ floatx16 mfma(const u32x4& x, const u32x4& y, const f
 // ---------------------------------------------------------------------------
 
 // Epilogue of one wave: accumulator -> (GELU / ReLU) -> output type -> LDS staging ->
-// 16-byte row-contiguous global stores.  The stores are nontemporal: C is written once
-// and never read here, and at the end of each round of tiles every workgroup stores its
-// tile at once (32 MiB at 8192^3), which with the default policy evicts A/B panel
-// lines the next round still needs (measured at 8192^3: NN -2.0%, TN -3.7% time).  The wave's C tile is processed in 32-row
+// 16-byte row-contiguous global stores.  Where C's rows are whole 128-byte cache lines
+// apart the stores are nontemporal: C is written once and never read here, and at the
+// end of each round of tiles every workgroup stores its tile at once (32 MiB at 8192^3),
+// which with the default policy evicts A/B panel lines the next round still needs
+// (measured at 8192^3: NN -2.0%, TN -3.7% time).  Where they are not (N = 5000 with an
+// fp32 C: rows 20,000 bytes apart), a tile's row segments share their first and last
+// cache line with the neighbouring tiles; nontemporal writes of such partial lines are
+// not merged, and there the default policy, which merges them in L2, is faster
+// (3000x5000x1000 fp16 -> fp32: 45.4 -> 40.2 us; fp16 out 39.8 -> 36.3 us; 5000x3000 ->
+// fp32 64.2 -> 59.7 us; shapes with line-multiple rows unchanged).  The wave's C tile is processed in 32-row
 // blocks (one MFMA block row), NP blocks per round: a round writes its blocks into NP
 // private 32 x WN staging buffers, then reads them back row by row and stores them, so
 // the LDS write -> read -> store latency is paid once per round rather than per block.
@@ -301,6 +307,7 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TN][TM], char* 
     const int M = args.M, N = args.N;
     // 16-byte stores need 16-byte rows and a 16-byte aligned C; otherwise element stores
     const bool vec_ok = (N % E16) == 0 && args.c_align >= 16;
+    const bool nt_rows = ((size_t)N * OB) % 128 == 0;   // see the comment above
     const int lrow = lane & 31;
 #pragma unroll
     for (int g = 0; g < TM; g += NP) {
@@ -354,7 +361,8 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TN][TM], char* 
                 if (gm < M && gn < N) {
                     char* dstg = (char*)args.C + ((size_t)gm * N + gn) * OB;
                     if (vec_ok && gn + E16 <= N) {
-                        __builtin_nontemporal_store(val, (u32x4*)dstg);
+                        if (nt_rows) __builtin_nontemporal_store(val, (u32x4*)dstg);
+                        else *(u32x4*)dstg = val;
                     } else {
                         const int lim = (N - gn) < E16 ? (N - gn) : E16;
                         for (int e = 0; e < lim; ++e) {
@@ -385,6 +393,7 @@ __device__ __forceinline__ void store_tile16(const floatx4 (&acc)[TN][TM], char*
     auto swz = [](int row) { return CPR >= 16 ? (row & 15) : ((row >> 1) & 7); };
     const int M = args.M, N = args.N;
     const bool vec_ok = (N % E16) == 0 && args.c_align >= 16;
+    const bool nt_rows = ((size_t)N * OB) % 128 == 0;   // the store policy of store_tile
     const int lrow = lane & 15;
 #pragma unroll
     for (int g = 0; g < NB32; g += NP) {
@@ -431,7 +440,8 @@ __device__ __forceinline__ void store_tile16(const floatx4 (&acc)[TN][TM], char*
                 if (gm < M && gn < N) {
                     char* dstg = (char*)args.C + ((size_t)gm * N + gn) * OB;
                     if (vec_ok && gn + E16 <= N) {
-                        __builtin_nontemporal_store(val, (u32x4*)dstg);
+                        if (nt_rows) __builtin_nontemporal_store(val, (u32x4*)dstg);
+                        else *(u32x4*)dstg = val;
                     } else {
                         const int lim = (N - gn) < E16 ? (N - gn) : E16;
                         for (int e = 0; e < lim; ++e) {
