@@ -43,7 +43,7 @@ class Workload:
     in_dtype: str
     out_dtype: str
     b_layout: str
-    epilogue: str  # "none" | "gelu_tanh"
+    epilogue: str  # "none" | "gelu_tanh" | "relu"
     dist: Tuple  # ("uniform", lo, hi) | ("normal", sigma) | ("unit",) == uniform [0, 1)
 
     @property
@@ -52,7 +52,7 @@ class Workload:
 
     def describe(self) -> str:
         lay = "B[K,N] (NN)" if self.b_layout == B_KN else "B[N,K] (transpose_B)"
-        epi = ", fused tanh-GELU" if self.epilogue != "none" else ""
+        epi = {"none": "", "gelu_tanh": ", fused tanh-GELU", "relu": ", fused ReLU"}[self.epilogue]
         return (f"{self.in_dtype} GEMM M={self.M} N={self.N} K={self.K}, A[M,K], {lay}, "
                 f"inputs {self.dist}, fp32 accumulate, {self.out_dtype} output{epi}")
 
