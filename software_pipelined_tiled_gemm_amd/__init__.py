@@ -18,6 +18,10 @@ from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspgemm.so")
+# The poison library: the same C ABI built with -DSPG_POISON from a subset of the
+# configurations, every released ring region overwritten with NaN (a race detector
+# for the GPU tests; build.build_poison()).
+POISON_LIB_PATH = os.path.join(_HERE, "libspgemm_poison.so")
 
 GEMM_OK = 0
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "out of memory",
@@ -76,15 +80,28 @@ EXPORTED = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_get_config", "gemm_
             "gemm_last_hip_error", "gemm_wait_timeouts", "gelu_run")
 
 _lib = None
+_poison_lib = None
 
 
 def lib():
     """Load libspgemm.so (raises GemmError if it is missing: no fallback path exists)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise GemmError(5, f"HIP library {LIB_PATH} is not built (run __graft_entry__.build())")
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+def poison_lib():
+    """Load libspgemm_poison.so, the race-detecting test build of the same C ABI."""
+    global _poison_lib
+    if _poison_lib is None:
+        _poison_lib = _load(POISON_LIB_PATH)
+    return _poison_lib
+
+
+def _load(path):
+    if not os.path.exists(path):
+        raise GemmError(5, f"HIP library {path} is not built (run __graft_entry__.build())")
     # PyTorch-ROCm ships its own libamdhip64 / libhsa-runtime64.  Load it first so this
     # library binds (by soname) to that same HIP runtime instead of a second copy from
     # /opt/rocm: two HIP runtimes in one process do not share devices.
@@ -92,7 +109,7 @@ def lib():
         import torch  # noqa: F401
     except ImportError:
         pass
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     L.gemm_create.restype = ctypes.c_int
     L.gemm_create.argtypes = [ctypes.POINTER(vp), i64, i64, i64, ctypes.c_int, ctypes.c_int,
@@ -121,7 +138,6 @@ def lib():
     L.gemm_wait_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32]
     L.gelu_run.restype = ctypes.c_int
     L.gelu_run.argtypes = [vp, vp, i64, ctypes.c_int, vp]
-    _lib = L
     return L
 
 

@@ -20,6 +20,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libspgemm.so")
+POISON_OUT = os.path.join(HERE, "libspgemm_poison.so")
+# Units of the poison library (a test instrument: -DSPG_POISON turns the ring's released
+# regions into NaN; see kPoison in csrc/gemm_kernels.hpp): every direct-to-LDS ring
+# (S = 2..5 with 32x32x16, the 16x16x32 tiles, the A-deep and B-deep rings, release
+# delay 1, persistent tiles) and the register-staged misaligned mode, which also
+# covers every configuration the shape heuristic picks.
+POISON_UNITS = (8, 14, 23, 24, 25, 26, 27, 28, 30, 31, 32)
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in any generated code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -42,12 +49,16 @@ def units() -> list:
     return sorted(found)
 
 
-def build(out: str = OUT, extra=()) -> str:
+def build(out: str = OUT, extra=(), poison: bool = False) -> str:
+    """Compile the library; poison=True builds the poison library from POISON_UNITS."""
     unit_src = os.path.join(CSRC, "gemm_unit.hip")
+    us = [u for u in units() if u in POISON_UNITS] if poison else units()
+    keep = [f"-DSPG_KEEP_{u}=~,1" for u in us] if poison else []
+    pdef = ["-DSPG_POISON"] if poison else []
     # (source, object name, defines): the host side, the GELU, and one object per unit
-    jobs = [(os.path.join(CSRC, "gemm.hip"), "gemm.o", []),
+    jobs = [(os.path.join(CSRC, "gemm.hip"), "gemm.o", pdef + keep),
             (os.path.join(CSRC, "gelu.hip"), "gelu.o", [])]
-    jobs += [(unit_src, f"gemm_unit{u}.o", [f"-DSPG_UNIT_IS_{u}=~,1"]) for u in units()]
+    jobs += [(unit_src, f"gemm_unit{u}.o", pdef + [f"-DSPG_UNIT_IS_{u}=~,1"]) for u in us]
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     with tempfile.TemporaryDirectory(prefix="spgemm_build_") as tmp:
         def compile_one(job):
@@ -66,5 +77,12 @@ def build(out: str = OUT, extra=()) -> str:
     return out
 
 
+def build_poison(out: str = POISON_OUT) -> str:
+    return build(out, poison=True)
+
+
 if __name__ == "__main__":
-    print(build(*sys.argv[1:2]))
+    if sys.argv[1:2] == ["--poison"]:
+        print(build_poison())
+    else:
+        print(build(*sys.argv[1:2]))

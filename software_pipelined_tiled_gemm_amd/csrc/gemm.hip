@@ -61,17 +61,32 @@ struct Variant {
 
 #define SPG_LP(BF, NK, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED, PERS, MI) \
     launch_pipelined<BF, NK, BM, BN, BK, WM, WN, S, (SWZ != 0), LDM, PF, SCHED, (PERS != 0), MI>
-#define SPG_V(unit, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED, PERS, MI)                          \
+#define SPG_ENTRY(BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED, PERS, MI)                            \
     Variant{{BM, BN, BK, S, WM, WN, SWZ, 0, 1, LDM, PF, SCHED, PERS, 0, MI},                       \
             {{SPG_LP(false, false, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED, PERS, MI),         \
               SPG_LP(false, true, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED, PERS, MI)},         \
              {SPG_LP(true, false, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED, PERS, MI),          \
               SPG_LP(true, true, BM, BN, BK, WM, WN, S, SWZ, LDM, PF, SCHED, PERS, MI)}}},
+#ifdef SPG_POISON
+// The poison library (a test build, see kPoison) holds only the units its build names
+// with -DSPG_KEEP_<n>=~,1; the table lists the lines of those units.
+#define SPG_CAT_(a, b) a##b
+#define SPG_CAT(a, b) SPG_CAT_(a, b)
+#define SPG_SECOND_(a, b, ...) b
+#define SPG_SECOND(...) SPG_SECOND_(__VA_ARGS__)
+#define SPG_KEPT(u) SPG_SECOND(SPG_CAT(SPG_KEEP_, u), 0)
+#define SPG_VK_0(...)
+#define SPG_VK_1(...) SPG_ENTRY(__VA_ARGS__)
+#define SPG_V(unit, ...) SPG_CAT(SPG_VK_, SPG_KEPT(unit))(__VA_ARGS__)
+#else
+#define SPG_V(unit, ...) SPG_ENTRY(__VA_ARGS__)
+#endif
 
 const Variant kVariants[] = {
 #include "variants.inc"
 };
 #undef SPG_V
+#undef SPG_ENTRY
 #undef SPG_LP
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 constexpr int kDefaultGroupM = 4;

@@ -506,6 +506,21 @@ constexpr int blocks_per_round(int budget) {
     return np;
 }
 
+// Poisoned ring (a test instrument, compiled only into the separate poison library with
+// -DSPG_POISON): the ring starts as NaN, and the moment the barrier protocol releases a
+// region of a slot, the wave that will refill it first overwrites it with NaN (all-ones
+// halves: NaN in both fp16 and bf16).  A fragment read that the protocol does not cover,
+// of a k-tile whose copies have not landed and been published, or of a slot already
+// released, then reads NaN rather than a plausible stale or early k-tile, the NaN reaches
+// every output of the MFMA tile, and a parity test cannot miss it.  The write-after-read
+// window widens from "until the refill lands" (hundreds of cycles) to "from the release
+// barrier on".
+#ifdef SPG_POISON
+constexpr bool kPoison = true;
+#else
+constexpr bool kPoison = false;
+#endif
+
 // Workgroup barrier for LDS hazards only: this wave's LDS operations have
 // completed (lgkmcnt(0)) and every wave has arrived.  Unlike __syncthreads it
 // does not wait for outstanding global loads, so staged loads stay in flight.
@@ -697,6 +712,24 @@ pipelined_gemm(KArgs args) {
     const int wm = wave / G::WAVES_N;
     const int wn = wave % G::WAVES_N;
 
+    constexpr u32x4 kNaN16 = {~0u, ~0u, ~0u, ~0u};
+    if constexpr (kPoison) {
+        // the poison build: every slot starts as NaN
+        auto fill = [&](char* p, int bytes) {
+            for (int o = tid * 16; o < bytes; o += G::NT * 16) *(u32x4*)(p + o) = kNaN16;
+        };
+        // (only the arrays this configuration uses: touching a placeholder would allocate it)
+        fill(ring0, sizeof ring0);
+        if constexpr (S > 1) fill(ring1, sizeof ring1);
+        if constexpr (S > 2) fill(ring2, sizeof ring2);
+        if constexpr (S > 3) fill(ring3, sizeof ring3);
+        if constexpr (S > 4) fill(ring4, sizeof ring4);
+        if constexpr (S > 5) fill(ring5, sizeof ring5);
+        if constexpr (LDM == 4) fill(ring_a2, sizeof ring_a2);
+        if constexpr (LDM == 6) fill(ring_b2, sizeof ring_b2);
+        __syncthreads();
+    }
+
     int tm, tn;
     tile_of(blockIdx.x, args, tm, tn);
     const int M = args.M, N = args.N, K = args.K;
@@ -884,6 +917,18 @@ pipelined_gemm(KArgs args) {
     auto issue = [&](const Slot& slot, int kt, auto first) __attribute__((always_inline)) {
         const DmaSrc src = dma_src(kt);
         static_for<0, G::L>([&](auto jc) { dma_op(slot, src, jc, first); });
+    };
+    // the poison build: NaN over every region of `slot` that this wave's copy ops write.
+    // Direct-to-LDS copies write the LDS outside the wave's LDS queue, so the NaN must
+    // have landed (lgkmcnt(0)) before they are issued; a register-staged refill is an
+    // LDS write of the same wave, which the LDS executes in order after the NaN.
+    auto poison_slot = [&](const Slot& slot) __attribute__((always_inline)) {
+        if constexpr (kPoison) {
+            static_for<0, G::L>([&](auto jc) {
+                *(SPG_LDS u32x4*)(part(slot, jc) + lds_off(jc) + lane * 16) = kNaN16;
+            });
+            if constexpr (!REG) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
     };
 
     // ---- persistent: the copy side of the k-tile stream ------------------------
@@ -1169,6 +1214,7 @@ pipelined_gemm(KArgs args) {
                 kstage(kc, r0, none, none, kNoCopy, std::integral_constant<int, -1>{}, RD{});
             });
             __syncthreads();
+            poison_slot(r0);
             issue(r0, t + 1, NotFirst{});  // past the last k-tile: zeros
         }
     } else {
@@ -1283,6 +1329,9 @@ pipelined_gemm(KArgs args) {
             // 16x16x32, where no raised priority, dropping it part-way through the stage
             // or raising it before the barrier instead were all slower).
             __builtin_amdgcn_s_setprio(1);
+            // the poison build: the regions released here (released at the previous
+            // barrier, with release delay 1) become NaN before their refill is issued
+            poison_slot(LDM == 5 ? prev : cur);
             {
                 // the window that starts here: k-tile t+S into cur
                 // (register staging: write k-tile t+S, load k-tile t+S+1)

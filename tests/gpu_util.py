@@ -38,6 +38,13 @@ def c_values(C, w: W.Workload, rows=None) -> np.ndarray:
     return oracle.decode(h.view(np.uint16), w.out_dtype)
 
 
+def c_values_raw(raw: np.ndarray, w: W.Workload) -> np.ndarray:
+    """Host copy of C (int16 bits or float32) -> float64 values."""
+    if w.out_dtype == W.F32:
+        return raw.astype(np.float64)
+    return oracle.decode(raw.view(np.uint16), w.out_dtype)
+
+
 def run(w: W.Workload, a_bits, b_bits, force=None, C=None, autotune=False):
     import torch
     A, B = to_dev(a_bits), to_dev(b_bits)

@@ -42,6 +42,25 @@ def test_every_declared_symbol_is_exported(L):
         assert hasattr(L, n), n
 
 
+def test_poison_library_exports_the_same_abi():
+    # the race-detecting test build: same entry points, a subset of the configurations,
+    # every one of which the production library also holds
+    if not os.path.exists(spg.POISON_LIB_PATH):
+        pytest.fail("libspgemm_poison.so is not built; run __graft_entry__.build()")
+    P = spg.poison_lib()
+    for n in declared_functions():
+        assert hasattr(P, n), n
+    def cfgs(lib):
+        out = []
+        for i in range(lib.gemm_num_configs()):
+            c = spg.TileConfig()
+            assert lib.gemm_list_config(i, ctypes.byref(c)) == 0
+            out.append(tuple(sorted(c.as_dict().items())))
+        return out
+    poison, prod = cfgs(P), set(cfgs(spg.lib()))
+    assert 0 < len(poison) < len(prod) and set(poison) <= prod
+
+
 def test_status_strings(L):
     for code, text in spg.STATUS.items():
         assert spg.gemm_status_string(code) == text

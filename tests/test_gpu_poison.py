@@ -1,0 +1,160 @@
+"""The poisoned ring on the GPU: libspgemm_poison.so is the same C ABI built with
+-DSPG_POISON, in which each LDS region of the ring is overwritten with NaN the moment
+the barrier protocol releases it (and the whole ring starts as NaN).  A fragment read
+that the protocol does not cover -- a slot read before its copies landed and were
+published at a barrier, or after it was released for a refill -- then feeds NaN into
+the MFMA tile instead of a plausible stale or early k-tile, so a premature slot reuse
+cannot hide behind timing that happens to work.
+
+Each case runs a configuration of the poison library and the same configuration of the
+production library on the same inputs: the poison result has no NaN, equals the
+production result bit for bit, and meets the oracle's tolerance (on the shapes the
+oracle finishes quickly).  The cases cover every ring the poison library holds (direct
+copies with S = 2..5, the A-deep and B-deep rings, release delay 1, persistent tiles,
+register-staged copies of misaligned rows), 1 to 13 k-tiles, grids of more tiles than
+CUs, and the full-size 8192^3 runs in the configuration the heuristic picks.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import software_pipelined_tiled_gemm_amd as spg
+import workloads as W
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _configs(L):
+    out = []
+    for i in range(L.gemm_num_configs()):
+        c = spg.TileConfig()
+        assert L.gemm_list_config(i, ctypes.byref(c)) == 0
+        out.append(c)
+    return out
+
+
+def _run(L, w, A, B, C, force=None):
+    """One launch through library L's C ABI; returns the configuration it ran."""
+    import torch
+    h = ctypes.c_void_p()
+    st = L.gemm_create(ctypes.byref(h), w.M, w.N, w.K, spg.DTYPES[w.in_dtype],
+                       spg.DTYPES[w.out_dtype], spg.B_LAYOUTS[w.b_layout],
+                       spg.EPILOGUES[w.epilogue], ctypes.byref(force) if force is not None else None)
+    assert st == 0, (st, w.describe(), force)
+    try:
+        stream = torch.cuda.current_stream().cuda_stream
+        assert L.gemm_run(h, A.data_ptr(), B.data_ptr(), C.data_ptr(), stream) == 0
+        cfg = spg.TileConfig()
+        assert L.gemm_get_config(h, ctypes.byref(cfg)) == 0
+    finally:
+        L.gemm_destroy(h)
+    torch.cuda.synchronize()
+    return cfg
+
+
+def _raw(C):
+    return C.cpu().numpy().copy()
+
+
+def _nan_count(raw, w):
+    vals = raw.astype(np.float64) if w.out_dtype == W.F32 else G.c_values_raw(raw, w)
+    return int(np.isnan(vals).sum())
+
+
+def _poison_vs_production(w, a, b, force=None, oracle=True):
+    A, B = G.to_dev(a), G.to_dev(b)
+    Cp, Cr = G.alloc_c(w, 0), G.alloc_c(w, 0)
+    cfg = _run(spg.poison_lib(), w, A, B, Cp, force)
+    _run(spg.lib(), w, A, B, Cr, force if force is not None else cfg)
+    p, r = _raw(Cp), _raw(Cr)
+    nans = _nan_count(p, w)
+    assert nans == 0, f"{nans} NaN outputs: a poisoned LDS region was read ({cfg}, {w.describe()})"
+    assert np.array_equal(p.view(np.uint8), r.view(np.uint8)), (cfg, w.describe())
+    if oracle:
+        G.check(w, a, b, G.c_values(Cp, w))
+    return cfg
+
+
+def test_poison_library_holds_the_rings():
+    cfgs = _configs(spg.poison_lib())
+    stagings = {c.staging for c in cfgs}
+    stages = {c.stages for c in cfgs if c.staging == 0}
+    assert {0, 4, 5, 6, 7} <= stagings, stagings
+    assert {2, 3, 4, 5} <= stages, stages
+    assert any(c.persistent for c in cfgs) and {16, 32} <= {c.mfma for c in cfgs}
+    # the production library holds every one of them
+    prod = {tuple(sorted(c.as_dict().items())) for c in _configs(spg.lib())}
+    for c in cfgs:
+        assert tuple(sorted(c.as_dict().items())) in prod, c
+
+
+@pytest.mark.parametrize("in_dtype", [W.F16, W.BF16])
+@pytest.mark.parametrize("b_layout", [W.B_KN, W.B_NK])
+def test_every_poisoned_ring_ragged(in_dtype, b_layout):
+    # several tiles in M and N with ragged edges and a K tail (K % 64 = 40)
+    w = W.custom(520, 648, 616, in_dtype, in_dtype, b_layout, "none", ("uniform", -1.0, 1.0))
+    a, b = W.make_inputs(w)
+    aligned = [c for c in _configs(spg.poison_lib()) if c.staging != 7]
+    for cfg in aligned:
+        _log(f"poison {cfg} {w.describe()}")
+        _poison_vs_production(w, a, b, force=cfg)
+
+
+@pytest.mark.parametrize("b_layout", [W.B_KN, W.B_NK])
+def test_poisoned_rings_every_ktile_count(b_layout):
+    # 1 .. 13 k-tiles (K % 64 = 0 and ragged), so every ring position of the last k-tile,
+    # the deep rings' 6-k-tile unroll and its tail are all reached; the oracle checks one
+    # configuration per shape, the rest must equal the production library bitwise
+    cfgs = [c for c in _configs(spg.poison_lib()) if c.staging != 7]
+    for nk in range(1, 14):
+        for K in sorted({64 * nk, 64 * nk - 24}):
+            w = W.custom(264, 520, K, W.BF16, W.BF16, b_layout, "none", ("uniform", -1.0, 1.0))
+            a, b = W.make_inputs(w)
+            for i, cfg in enumerate(cfgs):
+                _log(f"poison K={K} {cfg}")
+                _poison_vs_production(w, a, b, force=cfg, oracle=(i == 0))
+
+
+@pytest.mark.parametrize("b_layout", [W.B_KN, W.B_NK])
+def test_poisoned_rings_more_tiles_than_cus(b_layout):
+    # 17 x 17 tiles of 256 x 256 (more than one round on 256 CUs), 10 k-tiles: the
+    # persistent ring streams two tiles per workgroup on some CUs
+    w = W.custom(4352, 4352, 640, W.F16, W.F16, b_layout, "none", ("uniform", -1.0, 1.0))
+    a, b = W.make_inputs(w)
+    for cfg in _configs(spg.poison_lib()):
+        if cfg.staging == 7 or cfg.block_k != 64:
+            continue
+        _log(f"poison {cfg} {w.describe()}")
+        _poison_vs_production(w, a, b, force=cfg, oracle=False)
+
+
+def test_poisoned_misaligned_rows():
+    # register-staged copies of rows that are not 16 bytes apart (copy mode 7)
+    for (M, N, K, lay) in ((300, 263, 200, W.B_KN), (300, 517, 100, W.B_NK), (129, 129, 129, W.B_KN)):
+        w = W.custom(M, N, K, W.F16, W.F16, lay, "none", ("uniform", -1.0, 1.0))
+        a, b = W.make_inputs(w)
+        for cfg in _configs(spg.poison_lib()):
+            if cfg.staging != 7:
+                continue
+            _log(f"poison {cfg} {w.describe()}")
+            _poison_vs_production(w, a, b, force=cfg)
+
+
+@pytest.mark.parametrize("name", ["nn_f16_8192", "nn_bf16_8192"])
+def test_poisoned_full_size_default(name):
+    # the benchmark's 8192^3 problem in the configuration the heuristic picks (the
+    # B-deep ring with B stored [K,N]), and the same inputs with B stored [N,K]
+    w0 = W.WORKLOADS[name]
+    for lay in (W.B_KN, W.B_NK):
+        w = W.custom(w0.M, w0.N, w0.K, w0.in_dtype, w0.out_dtype, lay, "none", w0.dist)
+        a, b = W.make_inputs(w)
+        _log(f"poison full size {w.describe()}")
+        cfg = _poison_vs_production(w, a, b, oracle=False)
+        _log(f"  ran {cfg}")
