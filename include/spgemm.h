@@ -192,10 +192,11 @@ gemm_status gemm_launch_config(gemm_handle h, const void* A, const void* B, cons
                                gemm_tile_config* out);
 
 /* Time every compiled configuration that fits the plan's problem on the caller's
- * buffers (C is overwritten), `reps` launches each after one warm-up, and make the
- * fastest the plan's configuration; also remembered for later gemm_create calls
- * with the same problem in this process.  Synchronizes `stream`.  best_us (may be
- * NULL) receives the winner's mean time per launch in microseconds. */
+ * buffers, `reps` launches each after one warm-up, and make the fastest the plan's
+ * configuration; also remembered for later gemm_create calls with the same problem in
+ * this process.  C is overwritten: on return it holds the product as the last
+ * configuration timed computed it (within the same tolerance).  Synchronizes `stream`.
+ * best_us (may be NULL) receives the winner's mean time per launch in microseconds. */
 gemm_status gemm_autotune(gemm_handle h, const void* A, const void* B, void* C,
                           hipStream_t stream, int reps, double* best_us);
 

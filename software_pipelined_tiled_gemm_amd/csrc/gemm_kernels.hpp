@@ -116,7 +116,11 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 // purpose: the compiler's wait-count pass cannot tell which LDS slot a DMA
 // writes, and would otherwise wait for every outstanding copy before any LDS
 // read, serializing the ring.  The kernel orders these copies itself with
-// s_waitcnt vmcnt(N) and the per-k-tile barrier.
+// s_waitcnt vmcnt(N) and the per-k-tile barrier.  The asm writes M0 and lists it as
+// clobbered; the compiler warns that M0 is a register it reserves.  These kernels
+// (built for gfx950, where LDS instructions do not read M0 and every register array
+// index is a compile-time constant) contain no M0 access of the compiler's own: in
+// their assembly every M0 write is the one in this asm, one per LDS-DMA load.
 __device__ __forceinline__ void dma16(const i32x4& rsrc, SPG_LDS char* lds_dst, uint32_t voff) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
     // s_nop: one wait state between the M0 write and the LDS-DMA load that reads it
