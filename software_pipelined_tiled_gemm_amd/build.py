@@ -24,9 +24,9 @@ POISON_OUT = os.path.join(HERE, "libspgemm_poison.so")
 # Units of the poison library (a test instrument: -DSPG_POISON turns the ring's released
 # regions into NaN; see kPoison in csrc/gemm_kernels.hpp): every direct-to-LDS ring
 # (S = 2..5 with 32x32x16, the 16x16x32 tiles, the A-deep and B-deep rings, release
-# delay 1, persistent tiles) and the register-staged misaligned mode, which also
-# covers every configuration the shape heuristic picks.
-POISON_UNITS = (8, 14, 23, 24, 25, 26, 27, 28, 30, 31, 32)
+# delay 1, persistent tiles), the wave-specialized ring and the register-staged
+# misaligned mode, which also covers every configuration the shape heuristic picks.
+POISON_UNITS = (8, 14, 21, 23, 24, 25, 26, 27, 28, 30, 31, 32)
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in any generated code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -1529,6 +1529,11 @@ ws_gemm(KArgs args) {
     const int pad = (BK - K % BK) % BK;
 
     if (threadIdx.x < S) { full[threadIdx.x] = 0; freed[threadIdx.x] = 0; }
+    if constexpr (kPoison) {
+        // the poison build: every slot starts as NaN
+        for (int o = threadIdx.x * 16; o < (int)sizeof ring; o += G::NT * 16)
+            *(u32x4*)(ring + o) = u32x4{~0u, ~0u, ~0u, ~0u};
+    }
     __syncthreads();
 
     SPG_LDS char* ring_l = (SPG_LDS char*)ring;
@@ -1603,7 +1608,18 @@ ws_gemm(KArgs args) {
         };
         issue(0, true);
         for (int t = 1; t < nk; ++t) {
-            if (t >= S) wait_at_least(&freed[t % S], (uint32_t)(NC * (t / S)), args.wait_timeouts);
+            if (t >= S) {
+                wait_at_least(&freed[t % S], (uint32_t)(NC * (t / S)), args.wait_timeouts);
+                if constexpr (kPoison) {
+                    // the poison build: the slot every consumer has released becomes NaN,
+                    // and that write lands before the copies that refill it are issued
+                    SPG_LDS char* dst = slot(t);
+#pragma unroll
+                    for (int j = 0; j < L; ++j)
+                        *(SPG_LDS u32x4*)(dst + j * 1024 + lane * 16) = u32x4{~0u, ~0u, ~0u, ~0u};
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                }
+            }
             issue(t, false);
             wait_vmcnt<L>();      // k-tile t-1 has landed
             publish(t - 1);
