@@ -1,5 +1,5 @@
 // Launchers of the pipelined kernel: declared for the host unit, defined and
-// explicitly instantiated by the gemm_tu<k>.hip units (see variants.inc).
+// explicitly instantiated by gemm_unit.hip, compiled once per unit number of variants.inc.
 #pragma once
 
 #include <hip/hip_runtime.h>
