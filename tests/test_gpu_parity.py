@@ -574,3 +574,45 @@ def test_gemm_run_replays_in_a_hip_graph(shape):
             assert torch.equal(C_graph, C_eager), f"replay {i}"
         del graph
     G.check(w, a, b, G.c_values(C_eager, w))
+
+
+def test_one_plan_on_two_streams():
+    """A plan is read-only after gemm_create, so one handle may run on several streams at
+    once.  Two streams (default priority) run the same plan back to back without any
+    synchronization between them: one on 16-byte aligned operands, the other on an A whose
+    base address is 2 bytes past a 16-byte boundary (the plan's register-staged twin).
+    Every launch gives its problem's single-stream result bitwise, and those results are
+    within tolerance of the oracle."""
+    import torch
+    M, N, K = 1000, 1096, 704
+    w = W.custom(M, N, K, W.F16, W.F16, W.B_NK, "none", ("uniform", -1.0, 1.0), name="two_streams")
+    a, b = W.make_inputs(w)
+    a2, b2 = W.make_inputs(w, seed_a=7, seed_b=8)
+    A1, B1 = G.to_dev(a), G.to_dev(b)
+    buf = torch.zeros(M * K + 8, dtype=torch.int16, device=G.torch_dev())
+    A2 = buf[1:1 + M * K].view(M, K)          # 2-byte aligned only
+    A2.copy_(G.to_dev(a2))
+    B2 = G.to_dev(b2)
+    with spg.Gemm(M, N, K, w.in_dtype, w.out_dtype, w.b_layout, w.epilogue) as g:
+        R1, R2 = G.alloc_c(w), G.alloc_c(w)
+        assert g.launch_config(A1, B1, R1).staging != 7
+        assert g.launch_config(A2, B2, R2).staging == 7
+        _log(f"two streams: {g.launch_config(A1, B1, R1)} and {g.launch_config(A2, B2, R2)}")
+        g(A1, B1, R1)
+        g(A2, B2, R2)
+        torch.cuda.synchronize()
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        s1.wait_stream(torch.cuda.current_stream())
+        s2.wait_stream(torch.cuda.current_stream())
+        C1 = [G.alloc_c(w, -1) for _ in range(4)]
+        C2 = [G.alloc_c(w, -1) for _ in range(4)]
+        torch.cuda.synchronize()
+        for i in range(4):
+            g(A1, B1, C1[i], s1)
+            g(A2, B2, C2[i], s2)
+        torch.cuda.synchronize()
+        for i in range(4):
+            assert torch.equal(C1[i], R1), f"stream 1, launch {i}"
+            assert torch.equal(C2[i], R2), f"stream 2, launch {i}"
+    G.check(w, a, b, G.c_values(R1, w))
+    G.check(w, a2, b2, G.c_values(R2, w))
