@@ -36,7 +36,7 @@ HEADLINE = "nn_f16_8192"
 # configuration first); the 256^3 one is a launch-latency case, not a roofline one.  The
 # last is the matmul + ReLU epilogue after the Triton lecture notes (2048x2048x1024 fp16
 # -> fp32; the notes give no size).
-CONFIG_LINES = ["nn_bf16_8192", "tn_f16_256", "tn_f16_4096", "tn_f16_3000x5000x1000_f32out",
+CONFIG_LINES = ["nn_bf16_8192", "tn_f16_8192", "tn_f16_256", "tn_f16_4096", "tn_f16_3000x5000x1000_f32out",
                 "nn_bf16_3072x4096x4096_gelu", "nn_f16_2048x2048x1024_relu_f32out"]
 
 
@@ -564,6 +564,7 @@ def parse_tile(spec):
 ABLATIONS = [
     ("default: 256x256x64, 8 waves of 128x64, 16x16x32 MFMAs, B one slot deeper than A (staging 6), compiler-placed schedule, group_m 4", "256x256x64:2:1:4:6:128x64:1:1:0:0:1:16"),
     ("the same with group_m 8 (the 32x32x16 kernel's best)", "256x256x64:2:1:8:6:128x64:1:1:0:0:1:16"),
+    ("the same ring under the ping-pong schedule (the two waves of a SIMD take turns; the default for B stored [N,K])", "256x256x64:2:1:4:6:128x64:1:2:0:0:1:16"),
     ("two-slot ring (S=2), hand-placed schedule: the base of the 16x16x32 rows below", "256x256x64:2:1:4:0:128x64:1:0:0:0:1:16"),
     ("16x16x32, no swizzle", "256x256x64:2:0:4:0:128x64:1:0:0:0:1:16"),
     ("16x16x32, no overlap (S=1, the serial loop)", "256x256x64:1:1:4:0:128x64:1:0:0:0:1:16"),

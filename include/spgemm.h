@@ -99,7 +99,7 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1, GEMM_EPI_RELU = 2 } ge
  *                       k-tiles to land and those of B one;
  *                       6 = as 4 with the roles swapped: B in a ring one slot
  *                       deeper than A (stages = 2: two A slots, three B slots);
- *                       compiled with schedule = 1 (16x16x32 tiles);
+ *                       compiled with schedule = 1 and 2 (16x16x32 tiles);
  *                       5 = as 0, with a slot refilled one k-tile after its release
  *                       (the Pallas guide's release delay of 1; stages >= 3): S-1
  *                       k-tiles in flight instead of S;
@@ -117,7 +117,12 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_TANH = 1, GEMM_EPI_RELU = 2 } ge
  *   schedule            0 = instructions of a stage placed by hand (each MFMA step
  *                       followed by its copy op and LDS reads, the TileLang
  *                       tutorial's manual stage/order placement); 1 = the same
- *                       instructions placed by the compiler (its planned pipeline)
+ *                       instructions placed by the compiler (its planned pipeline);
+ *                       2 = ping-pong (staging 6, 8 waves of 16x16x32 only): the two
+ *                       waves of each SIMD take turns, one issuing a k-step's MFMAs
+ *                       while the other reads the next fragments and copies, with a
+ *                       workgroup barrier between turns (a schedule of this library,
+ *                       not of the pages)
  *   persistent          1 = one workgroup per compute unit, each computing the tiles
  *                       g, g + G, g + 2G, ... (G = workgroups) as one continuous
  *                       pipeline of k-tiles, so the copies of a tile's first k-tiles

@@ -69,7 +69,7 @@ class TileConfig(ctypes.Structure):
                 f"wave {d['wave_m']}x{d['wave_n']}, swizzle={d['swizzle']}, "
                 f"group_m={d['group_m']}, xcd_remap={d['xcd_remap']}, "
                 f"staging={STAGING.get(d['staging'], d['staging'])}, lookahead={d['lookahead']}, "
-                f"schedule={'compiler' if d['schedule'] else 'manual'}"
+                f"schedule={('manual', 'compiler', 'ping-pong')[d['schedule']] if 0 <= d['schedule'] <= 2 else d['schedule']}"
                 f"{', persistent' if d['persistent'] else ''}{', direct store' if d['store'] else ''}"
                 f"{', mfma 16x16x32' if d['mfma'] == 16 else ''})")
 

@@ -248,15 +248,18 @@ gemm_tile_config heuristic(int64_t M, int64_t N, gemm_b_layout bl, bool aligned)
         const double t = (double)((tiles + cus - 1) / cus) * c.bm * c.bn / c.eff;
         if (!best || t < best_t) { best = &c; best_t = t; }
     }
-    // B stored [K,N] on grids of two rounds or more: the B-deep ring (staging 6, three B
-    // slots, compiler-placed schedule).  A [K,N] k-tile of B is 64 rows 2*N bytes apart,
-    // and its copies are the ones that land late: measured interleaved at 8192^3, bf16
-    // NN 710.0 -> 701.3 us, fp16 NN 753.6 -> 747.5 us; with B stored [N,K] it makes no
-    // difference (700.5 / 700.0 us).  Grids of one round keep the two-slot ring.
+    // Grids of two rounds or more on the 256x256 tile: the B-deep ring (staging 6, three
+    // B slots).  With B stored [K,N] under the compiler-placed schedule: a [K,N] k-tile
+    // of B is 64 rows 2*N bytes apart, and its copies are the ones that land late
+    // (measured interleaved at 8192^3, bf16 NN 710.0 -> 701.3 us, fp16 NN 753.6 ->
+    // 747.5 us).  With B stored [N,K] under the ping-pong schedule, which is 2-3% ahead
+    // of the two-slot hand-placed ring there in bf16 and ~1% in fp16, but ~2% behind the
+    // compiler-placed B-deep ring with B stored [K,N].  Grids of one round keep the
+    // two-slot ring (the ping-pong schedule is even there).
     const int64_t tiles = ((M + best->bm - 1) / best->bm) * ((N + best->bn - 1) / best->bn);
     const Variant* v = nullptr;
-    if (bl == GEMM_B_KN && best->bm == 256 && best->bn == 256 && tiles >= 2 * cus)
-        v = find_cfg(256, 256, 64, 2, 6, best->wm, best->wn, 0, 16, 1);
+    if (best->bm == 256 && best->bn == 256 && tiles >= 2 * cus)
+        v = find_cfg(256, 256, 64, 2, 6, best->wm, best->wn, 0, 16, bl == GEMM_B_KN ? 1 : 2);
     if (!v) v = find_cfg(best->bm, best->bn, best->bk, best->st, 0, best->wm, best->wn, 0, best->mfma);
     gemm_tile_config c = v->cfg;
     // 4 tile rows per raster group: with the 16x16x32 tiles at 8192^3 (32 tile rows),
@@ -432,7 +435,7 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
             (force->store != 0 && force->store != 1) ||
             (force->mfma != 0 && force->mfma != 16 && force->mfma != 32) ||
             (force->lookahead != 1 && force->lookahead != 2) ||
-            (force->schedule != 0 && force->schedule != 1) ||
+            force->schedule < 0 || force->schedule > 2 ||
             (force->persistent != 0 && force->persistent != 1))
             return GEMM_ERR_INVALID_ARG;
         if (gemm_lds_bytes(force) > 160 * 1024) return GEMM_ERR_UNSUPPORTED;

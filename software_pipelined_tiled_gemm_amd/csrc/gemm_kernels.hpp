@@ -16,30 +16,42 @@
 //    A buffer resource per operand makes every access past the end of the
 //    matrix return zero, which is how partial tiles read "other = 0"
 //    (the masked loads of the Triton matmul in the Triton lecture notes).
-//  * Each ring slot is its own __shared__ array and the K loop is unrolled by
-//    S, so every slot index is a compile-time constant.  The compiler can then
-//    prove that the LDS reads of slot t%S do not alias the DMA into slot
-//    (t+S-1)%S and does not insert a full `s_waitcnt vmcnt(0)` before them;
-//    the kernel waits for exactly the k-tile it needs with `vmcnt(N)`.
-//  * Delayed release (the guide's delay_release): slot (t-1)%S is refilled
-//    only after the one barrier of iteration t, i.e. one iteration after its
-//    last use.  MFMA reads registers, not LDS, so a slot is free once every
-//    wave's LDS reads of it have returned, which the barrier guarantees.  One
-//    barrier per k-tile suffices.
+//    Operands whose rows or base are not 16-byte aligned are staged through
+//    VGPRs instead (copy mode 7, any 2-byte alignment).
+//  * Each ring slot is its own __shared__ array and the K loop is unrolled over
+//    the slot pattern, so every slot index is a compile-time constant.  The
+//    compiler can then prove that the LDS reads of one slot do not alias the DMA
+//    into another and does not insert a full `s_waitcnt vmcnt(0)` before them;
+//    the kernel waits for exactly the copies it needs with `vmcnt(N)`.
+//  * One barrier per k-tile, placed right after each wave's last LDS read of the
+//    k-tile's slot, both publishes the next k-tile (every wave has waited for its
+//    own copies of it) and releases the slot (MFMA reads registers, not LDS, so a
+//    slot is free once every wave's reads of it have returned); the copies that
+//    refill it are issued right after that barrier.  The guide's delay_release of
+//    1 (refill one k-tile later) is copy mode 5.  B stored [K,N] on large grids
+//    gets one more B slot than A slots (mode 6), so its copies have two k-tiles
+//    to land.
 //  * LDS tiles are XOR-swizzled at 16-byte granularity (the "swizzling" the
 //    Triton notes give as the fix for bank conflicts, and the 128-byte swizzle
 //    of the Pallas example) so that the 64 lanes of an operand read hit
 //    distinct banks; the swizzle is applied by permuting the *global* chunk
 //    each lane fetches, because direct-to-LDS writes land at lane*16.
-//  * v_mfma_f32_32x32x16_{f16,bf16}; the B tile is the first MFMA operand and
-//    the A tile the second, so each lane's accumulator holds 4 consecutive
-//    output columns, which lets the epilogue pack 4 outputs per LDS write.
+//  * v_mfma_f32_16x16x32_{f16,bf16} on the default 8-wave tiles, v_mfma_f32_32x32x16
+//    on the 4-wave 128x128 tile and the misaligned-operand path (both shapes are
+//    compiled for the large tiles); the B tile is the first MFMA operand and the A
+//    tile the second,
+//    so each lane's accumulator holds consecutive output columns, which lets the
+//    epilogue pack 4 outputs per LDS write.
 //  * B stored [K,N] (N contiguous) is read with ds_read_b64_tr_b16, the
 //    gfx950 transposing LDS read, instead of being transposed in registers.
+//  * The instructions of a k-step are placed by hand, by the compiler, or (SCHED 2)
+//    as a ping-pong of the two waves of each SIMD: one multiplies while the other
+//    reads and copies, taking turns at a workgroup barrier.
 //  * Epilogue: optional GELU or ReLU on the fp32 accumulator, round-to-nearest-even
 //    conversion, staging through LDS (aliasing the drained ring), and 16-byte
 //    row-contiguous global stores (the coalesced linear output traversal of
-//    the XLA:GPU emitters page, loop emitter, with wider vectors).
+//    the XLA:GPU emitters page, loop emitter, with wider vectors), nontemporal
+//    where C's rows are whole cache lines apart.
 //  * Workgroup -> tile mapping gives each of the 8 XCDs a contiguous range of
 //    tiles and rasterises tiles in groups of `group_m` tile rows, so the
 //    workgroups that share an XCD's L2 share A and B panels.
@@ -624,7 +636,10 @@ __device__ __forceinline__ int kswz_t(int r) {
 // SCHED selects who places the instructions of a stage: 0 = by hand, every MFMA
 // step followed by its copy op and LDS reads and a scheduling barrier (the
 // TileLang tutorial's manual stage/order placement); 1 = the compiler, with the
-// same instructions and no scheduling barriers (its compiler-planned pipeline).
+// same instructions and no scheduling barriers (its compiler-planned pipeline);
+// 2 = ping-pong: the two waves of a SIMD take turns, one issuing only MFMAs while
+// the other reads fragments and copies, with a workgroup barrier between turns
+// (B-deep ring, 16x16x32, 8 waves; the K loop's comment has the protocol).
 //
 // PERS (persistent): the grid holds one workgroup per CU and workgroup w computes
 // tiles w, w + G, w + 2G, ... (G = grid size) as one continuous stream of k-tiles,
@@ -1287,7 +1302,9 @@ pipelined_gemm(KArgs args) {
             });
         }
         lds_barrier();
-        static_for<0, PF>([&](auto kc) { load_frags(slot_of(Z_{}), kc.value, fset(kc)); });
+        // (the ping-pong schedule reads its first fragments in its first memory phase)
+        if constexpr (SCHED != 2)
+            static_for<0, PF>([&](auto kc) { load_frags(slot_of(Z_{}), kc.value, fset(kc)); });
 
         // outstanding copies allowed at the wait before barrier t: k-tiles t+2 .. t+S-1
         // (in the A-deep ring, A of k-tile t+2; in the B-deep ring, B of k-tile t+2)
@@ -1371,7 +1388,83 @@ pipelined_gemm(KArgs args) {
                 }
             }
         };
-        if constexpr (PERS) {
+        if constexpr (SCHED == 2) {
+            // Ping-pong schedule.  A workgroup's waves are dealt to the 4 SIMDs in turn,
+            // so waves w and w+4 share a SIMD; waves 0..3 form group 0, waves 4..7 group
+            // 1.  Every wave alternates a memory phase -- the LDS reads of one k-step's
+            // fragments, and in the first k-step of a k-tile its copies into the slots
+            // the previous k-tile released -- with a matrix phase that issues that
+            // k-step's 32 MFMAs and nothing else.  Group 1 runs one phase behind group 0
+            // and a workgroup barrier ends every phase, so in each phase one wave of
+            // every SIMD multiplies from registers while its partner reads and copies;
+            // the multiplying wave never waits for the LDS.
+            //
+            // Phases are numbered from the end of the prologue.  Group 0 reads k-step j
+            // in phase 2j and multiplies it in phase 2j+1, group 1 one phase later, so
+            // k-tile u (k-steps 2u, 2u+1) is read in phases 4u .. 4u+3.  Each wave waits
+            // for its reads (lgkmcnt(0)) before the barrier that ends a memory phase, so
+            // k-tile u's slots are free once the barrier ending phase 4u+3 has passed.
+            // The first memory phase of k-tile u+1 (phase 4u+4 or 4u+5) copies A of
+            // k-tile u+2 and B of k-tile u+3 into them (the B-deep ring: A slots t % 2,
+            // B slots t % 3).  k-tile u+2 is first read in phase 4u+8; before the barrier
+            // that opens it each wave waits for its copies of A(u+2) and B(u+2), leaving
+            // only B(u+3) in flight: group 0 at the end of its matrix phase 4u+7, group 1
+            // at the end of its memory phase 4u+7.  Both groups pass the same number of
+            // barriers: group 1 one extra before its first phase, group 0 one after its
+            // last.
+            static_assert(LDM == 6 && S == 2 && MI == 16 && PF == 1 && G::NW == 8,
+                          "ping-pong: 8 waves of 16x16x32 tiles on the B-deep ring");
+            const int grp = wave >> 2;
+            // The scheduling barriers keep every MFMA inside its phase: MFMAs touch
+            // registers only, and the compiler would otherwise move them across the asm
+            // barrier into the memory phase.
+            auto phase_barrier = []() __attribute__((always_inline)) {
+                __builtin_amdgcn_sched_barrier(0);
+                asm volatile("s_barrier" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            Frags f;
+            auto matrix_phase = [&]() __attribute__((always_inline)) {
+                static_for<0, NMMA>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    mfma_step(f.b[i / TM], f.a[i % TM], acc[i / TM][i % TM]);
+                });
+            };
+            auto ktile_pp = [&](auto ic, int u) __attribute__((always_inline)) {
+                constexpr int i = decltype(ic)::value;
+                const Slot cur = deep_slot(std::integral_constant<int, i>{});
+                const Slot prev = deep_slot(std::integral_constant<int, (i + 5) % 6>{});
+                // k-step 2u: fragments, then (u >= 1) the copies of A(u+1), B(u+2)
+                load_frags(cur, 0, f);
+                if (u >= 1) {
+                    poison_slot(prev);
+                    const DmaSrc src{dma_src(u + 1).a, dma_src(u + 2).b};
+                    static_for<0, G::L>([&](auto jc) { dma_op(prev, src, jc, NotFirst{}); });
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                phase_barrier();
+                matrix_phase();
+                phase_barrier();
+                // k-step 2u+1; A(u+1) and B(u+1) complete before k-tile u+1 is read
+                load_frags(cur, 1, f);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                if (grp == 1) wait_vmcnt<B_DMA>();
+                phase_barrier();
+                matrix_phase();
+                if (grp == 0) wait_vmcnt<B_DMA>();
+                phase_barrier();
+            };
+            if (grp == 1) phase_barrier();
+            int t0 = 0;
+            for (; t0 + 6 <= nk; t0 += 6) {
+                static_for<0, 6>([&](auto sc) { ktile_pp(sc, t0 + decltype(sc)::value); });
+            }
+            const int rem = nk - t0;
+            static_for<0, 5>([&](auto sc) {
+                if (decltype(sc)::value < rem) ktile_pp(sc, t0 + decltype(sc)::value);
+            });
+            if (grp == 0) phase_barrier();
+        } else if constexpr (PERS) {
             // this workgroup's tiles as one stream of k-tiles, in whole S-groups (the
             // k-tiles past its last tile are zeros and nothing is stored for them)
             const int mine = (T - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;

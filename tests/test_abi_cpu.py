@@ -153,10 +153,19 @@ def test_forced_configs(L):
         spg.gemm_create(512, 512, 512, force=neg)
     assert e.value.status == 1
     sch = spg.TileConfig(block_m=256, block_n=256, block_k=64, stages=2, wave_m=128,
-                         wave_n=64, swizzle=1, group_m=4, xcd_remap=1, schedule=2)
+                         wave_n=64, swizzle=1, group_m=4, xcd_remap=1, schedule=3)
     with pytest.raises(spg.GemmError) as e:
         spg.gemm_create(512, 512, 512, force=sch)
     assert e.value.status == 1
+    # the ping-pong schedule is compiled for the B-deep ring only
+    sch.schedule = 2
+    with pytest.raises(spg.GemmError) as e:
+        spg.gemm_create(512, 512, 512, force=sch)
+    assert e.value.status == 2
+    sch.staging, sch.mfma = 6, 16
+    h = spg.gemm_create(512, 512, 512, force=sch)
+    assert spg.gemm_get_config(h).schedule == 2
+    spg.gemm_destroy(h)
     per = spg.TileConfig(block_m=256, block_n=256, block_k=64, stages=2, wave_m=128,
                          wave_n=64, swizzle=1, group_m=4, xcd_remap=1, persistent=2)
     with pytest.raises(spg.GemmError) as e:
@@ -290,7 +299,8 @@ def test_heuristic_tiles(L):
     h = spg.gemm_create(8192, 8192, 8192, "bf16", "bf16", "nk")
     tn = spg.gemm_get_config(h)
     spg.gemm_destroy(h)
-    assert (tn.block_m, tn.block_n, tn.mfma, tn.staging, tn.schedule) == (256, 256, 16, 0, 0)
+    # B stored [N,K] on a grid of several rounds: the same ring under the ping-pong schedule
+    assert (tn.block_m, tn.block_n, tn.mfma, tn.staging, tn.schedule) == (256, 256, 16, 6, 2)
     one_round = cfg(4096, 4096, 4096)
     assert (one_round.staging, one_round.schedule) == (0, 0)
     assert cfg(1024, 8192, 8192).mfma == 16 and cfg(256, 256, 256).mfma == 32

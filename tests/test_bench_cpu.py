@@ -55,7 +55,7 @@ def test_headline_is_the_metric_workload(bench):
         assert name in W.WORKLOADS and name != bench.HEADLINE
 
 
-@pytest.mark.parametrize("name", ["nn_f16_8192", "nn_bf16_8192", "tn_f16_4096",
+@pytest.mark.parametrize("name", ["nn_f16_8192", "nn_bf16_8192", "tn_f16_8192", "tn_f16_4096",
                                   "tn_f16_3000x5000x1000_f32out", "nn_bf16_3072x4096x4096_gelu",
                                   "nn_f16_2048x2048x1024_relu_f32out"])
 def test_configuration_line_and_roofline(bench, name):

@@ -330,7 +330,7 @@ def test_deep_ring_every_tail(staging):
     # one: every remainder 0..5, fewer k-tiles than one iteration, a leading partial
     # k-tile, both layouts; bitwise equal to the two-deep ring of the same tile, MFMA
     # shape and schedule (same k order) and within tolerance
-    deep = [c for c in _variants() if c.staging == staging]
+    deep = [c for c in _variants() if c.staging == staging and c.schedule != 2]
     assert deep, f"no staging-{staging} configuration compiled"
     d = deep[0]
     twin = [c for c in _variants() if c.staging == 0 and (c.block_m, c.block_n, c.block_k, c.stages,
@@ -353,7 +353,7 @@ def test_deep_ring_every_tail(staging):
 def test_b_deep_ring_epilogues_and_outputs():
     # the default kernel for B stored [K,N] on large grids: every output type and
     # epilogue on a ragged shape, against the oracle and bitwise against its two-slot twin
-    deep = [c for c in _variants() if c.staging == 6][0]
+    deep = [c for c in _variants() if c.staging == 6 and c.schedule != 2][0]
     twin = [c for c in _variants() if c.staging == 0 and (c.block_m, c.block_n, c.block_k, c.stages,
             c.wave_m, c.wave_n, c.lookahead, c.schedule, c.mfma) ==
             (deep.block_m, deep.block_n, deep.block_k, deep.stages, deep.wave_m, deep.wave_n,
@@ -457,7 +457,7 @@ def test_autotune_keeps_parity():
 
 FULL = ["tn_f16_256", "tn_f16_3000x5000x1000_f32out", "pallas_hopper_example",
         "nn_f16_2048x2048x1024_relu_f32out",
-        "tn_f16_4096", "nn_bf16_3072x4096x4096_gelu", "nn_bf16_8192", "nn_f16_8192"]
+        "tn_f16_4096", "nn_bf16_3072x4096x4096_gelu", "nn_bf16_8192", "nn_f16_8192", "tn_f16_8192"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -519,6 +519,62 @@ def test_b_deep_ring_bitwise_at_full_size(in_dtype):
     C1, _ = G.run(w, a, b)
     C2, used = G.run(w, a, b, force=twin)
     assert used.staging == 0
+    assert torch.equal(C1, C2)
+
+
+def _ping_pong_and_twin():
+    """The ping-pong configuration and its twin: the same B-deep ring, tile and MFMA shape
+    under the compiler-placed schedule.  Both give each accumulator its k-steps in the same
+    order, so their results are bitwise equal."""
+    pp = [c for c in _variants() if c.schedule == 2]
+    assert len(pp) == 1 and pp[0].staging == 6 and pp[0].mfma == 16, pp
+    pp = pp[0]
+    twin = [c for c in _variants() if c.schedule == 1 and c.staging == 6 and
+            (c.block_m, c.block_n, c.block_k, c.stages, c.wave_m, c.wave_n, c.mfma) ==
+            (pp.block_m, pp.block_n, pp.block_k, pp.stages, pp.wave_m, pp.wave_n, pp.mfma)]
+    assert twin, "no compiler-scheduled B-deep twin"
+    return pp, twin[0]
+
+
+def test_ping_pong_every_tail_and_epilogue():
+    """The ping-pong schedule (the two waves of each SIMD take turns at a workgroup barrier,
+    waves 4..7 one phase behind waves 0..3): fewer k-tiles than the six of one unrolled
+    iteration, every remainder, a leading partial k-tile, every output type and epilogue,
+    both layouts; within tolerance of the oracle and bitwise equal to its twin."""
+    pp, twin = _ping_pong_and_twin()
+    cases = [(K, W.BF16, W.BF16, "none") for K in (40, 64, 128, 192, 256, 320, 384, 448, 760, 1024)]
+    cases += [(1000, W.F16, W.F32, "gelu_tanh"), (448, W.F16, W.F16, "relu"), (520, W.BF16, W.BF16, "gelu_tanh")]
+    for K, in_dtype, out_dtype, epi in cases:
+        for layout in (W.B_KN, W.B_NK):
+            w = W.custom(300, 520, K, in_dtype, out_dtype, layout, epi, ("uniform", -1.0, 1.0))
+            a, b = W.make_inputs(w)
+            _log(f"ping-pong K={K} {w.describe()}")
+            C, used = G.run(w, a, b, force=pp)
+            assert used.schedule == 2
+            got = G.c_values(C, w)
+            G.check(w, a, b, got)
+            C2, _ = G.run(w, a, b, force=twin)
+            assert np.array_equal(G.c_values(C2, w), got)
+
+
+@pytest.mark.parametrize("in_dtype", [W.BF16, W.F16])
+def test_ping_pong_bitwise_at_full_size(in_dtype):
+    """B stored [N,K] at 8192^3: the heuristic's configuration is the ping-pong schedule;
+    its C equals its twin's bit for bit over all 67M elements (128 k-tiles per tile, four
+    rounds of tiles, where a turn taken out of order would show)."""
+    import torch
+    w = W.custom(8192, 8192, 8192, in_dtype, in_dtype, W.B_NK, "none", ("uniform", -1.0, 1.0),
+                 name=f"tn_{in_dtype}_8192")
+    a, b = W.make_inputs(w)
+    pp, twin = _ping_pong_and_twin()
+    with spg.Gemm(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.b_layout) as g:
+        planned = g.config()
+    assert planned.schedule == 2 and planned.staging == 6, planned
+    twin.group_m, twin.xcd_remap = planned.group_m, planned.xcd_remap
+    _log(f"ping-pong {planned} against {twin}: {w.describe()}")
+    C1, _ = G.run(w, a, b)
+    C2, used = G.run(w, a, b, force=twin)
+    assert used.schedule == 1
     assert torch.equal(C1, C2)
 
 

@@ -11,9 +11,9 @@ production library on the same inputs: the poison result has no NaN, equals the
 production result bit for bit, and meets the oracle's tolerance (on the shapes the
 oracle finishes quickly).  The cases cover every ring the poison library holds (direct
 copies with S = 2..5, the A-deep and B-deep rings, release delay 1, persistent tiles,
-the wave-specialized ring with its LDS counters, register-staged copies of misaligned
-rows), 1 to 13 k-tiles, grids of more tiles than CUs, and the full-size 8192^3 runs in
-the configuration the heuristic picks.
+the wave-specialized ring with its LDS counters, the ping-pong schedule, register-staged
+copies of misaligned rows), 1 to 13 k-tiles, grids of more tiles than CUs, and the
+full-size 8192^3 runs in the configuration the heuristic picks.
 """
 
 import ctypes
@@ -96,6 +96,7 @@ def test_poison_library_holds_the_rings():
     assert {0, 3, 4, 5, 6, 7} <= stagings, stagings
     assert {2, 3, 4, 5} <= stages, stages
     assert any(c.persistent for c in cfgs) and {16, 32} <= {c.mfma for c in cfgs}
+    assert any(c.schedule == 2 for c in cfgs)   # the ping-pong turns
     # the production library holds every one of them
     prod = {tuple(sorted(c.as_dict().items())) for c in _configs(spg.lib())}
     for c in cfgs:
@@ -159,7 +160,8 @@ def test_poisoned_misaligned_rows():
 @pytest.mark.parametrize("name", ["nn_f16_8192", "nn_bf16_8192"])
 def test_poisoned_full_size_default(name):
     # the benchmark's 8192^3 problem in the configuration the heuristic picks (the
-    # B-deep ring with B stored [K,N]), and the same inputs with B stored [N,K]
+    # B-deep ring with B stored [K,N]), and the same inputs with B stored [N,K] (the
+    # same ring under the ping-pong schedule)
     w0 = W.WORKLOADS[name]
     for lay in (W.B_KN, W.B_NK):
         w = W.custom(w0.M, w0.N, w0.K, w0.in_dtype, w0.out_dtype, lay, "none", w0.dist)

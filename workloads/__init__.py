@@ -78,6 +78,8 @@ WORKLOADS: Dict[str, Workload] = {
                  ("uniform", -1.0, 1.0)),
         # The same 8192^3 problem in fp16 (the metric's wording names fp16).
         Workload("nn_f16_8192", 8192, 8192, 8192, F16, F16, B_KN, "none", ("uniform", -1.0, 1.0)),
+        # ... and with B stored [N,K] (transpose_B, the other layout the pages use).
+        Workload("tn_f16_8192", 8192, 8192, 8192, F16, F16, B_NK, "none", ("uniform", -1.0, 1.0)),
     )
 }
 
