@@ -203,25 +203,27 @@ uint32_t* wait_word() {
     return p;
 }
 
-gemm_tile_config heuristic(int64_t M, int64_t N, gemm_b_layout bl, bool aligned) {
+gemm_tile_config heuristic(int64_t M, int64_t N, int64_t K, gemm_b_layout bl, bool aligned) {
     // Estimated time of a candidate = rounds of the device's CUs it needs x its tile's
     // area / its measured per-tile throughput relative to 256x256 (bf16 NN 8192^3
     // and the 1024x8192x8192 shard on MI355X: 256x128 runs at 0.91 of the 256x256
-    // rate per output, 128x128 at 0.66, 192x256 at 0.80 (3072x4096x4096) to 0.88
-    // (6144x8192x8192: 4 rounds of 192x256 against 3 of 256x256, 623 vs 549 us)).
+    // rate per output, 128x128 at 0.77 (8 waves of 16x16x32; 925 against 709 us at
+    // 8192^3), 192x256 at 0.80 (3072x4096x4096) to 0.88 (6144x8192x8192: 4 rounds of
+    // 192x256 against 3 of 256x256, 623 vs 549 us)).
     // The smallest estimate wins: 256x256 as long as the grid is not much less than
     // one round, 192x256 where its rows fill the CUs better (M = 3072: 16 x 16 tiles
     // against 12 x 16), 256x128 for half-size grids, 128x128 for small problems.
-    // The 8-wave tiles run 16x16x32 MFMAs (measured against 32x32x16 with the same
-    // tile, interleaved in one process, +2..9% on every benchmark shape; fp16 and
-    // [N,K] B gain the most), the 4-wave 128x128 tile 32x32x16.
+    // Every tile runs 8 waves of 16x16x32 MFMAs (measured against 32x32x16 with the
+    // same tile, interleaved in one process, +2..9% on every benchmark shape of the
+    // large tiles; 128x128 with 8 waves of 32x64 against 4 waves of 64x64 of 32x32x16:
+    // -10..-26% time on 256^3 .. 2048^3 and 1024x2048x4096).
     const int cc = cu_count();
     const int64_t cus = cc > 0 ? cc : 256;   // 256 on MI355X; also the planning default without a device
     struct Cand { int bm, bn, bk, st, wm, wn, mfma; double eff; };
     const Cand cands[] = {{256, 256, 64, 2, 128, 64, 16, 1.0},
                           {192, 256, 64, 2, 96, 64, 16, 0.85},
                           {256, 128, 64, 3, 64, 64, 16, 0.91},
-                          {128, 128, 64, 3, 64, 64, 32, 0.66}};
+                          {128, 128, 64, 3, 32, 64, 16, 0.77}};
     // Misaligned operands (copy mode 7, register-staged, 32x32x16): the same cost model
     // over the tiles compiled for that mode
     const Cand ucands[] = {{256, 256, 64, 2, 128, 64, 32, 1.0},
@@ -260,7 +262,15 @@ gemm_tile_config heuristic(int64_t M, int64_t N, gemm_b_layout bl, bool aligned)
     const Variant* v = nullptr;
     if (best->bm == 256 && best->bn == 256 && tiles >= 2 * cus)
         v = find_cfg(256, 256, 64, 2, 6, best->wm, best->wn, 0, 16, bl == GEMM_B_KN ? 1 : 2);
-    if (!v) v = find_cfg(best->bm, best->bn, best->bk, best->st, 0, best->wm, best->wn, 0, best->mfma);
+    // 128x128: S = 3 (96 KiB: one workgroup per CU) on grids of less than two rounds
+    // with more than 16 k-tiles, else S = 2 (64 KiB: two workgroups share a CU).
+    // Measured: 1024x2048x4096 (128 tiles) 24.9 us with S = 3 against 39.6 with S = 2,
+    // 2048^3 19.3 against 23.4; but 256^3 4.4 against 5.1 us, 1024^3 8.7 against 9.5,
+    // 2048x4096x4096 (512 tiles) 65.7 against 70.6, 8192^3 925 against 958.
+    int st = best->st;
+    if (best->bm == 128 && best->bn == 128)
+        st = (tiles < 2 * cus && (K + best->bk - 1) / best->bk > 16) ? 3 : 2;
+    if (!v) v = find_cfg(best->bm, best->bn, best->bk, st, 0, best->wm, best->wn, 0, best->mfma);
     gemm_tile_config c = v->cfg;
     // 4 tile rows per raster group: with the 16x16x32 tiles at 8192^3 (32 tile rows),
     // measured interleaved: group_m 2 / 4 / 8 / 16 / 32 = 758 / 730 / 740 / 752 / 911 us
@@ -454,7 +464,7 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
                 have = true;
             }
         }
-        if (!have) cfg = heuristic(M, N, b_layout, rows_aligned(N, K, b_layout));
+        if (!have) cfg = heuristic(M, N, K, b_layout, rows_aligned(N, K, b_layout));
         var = find_variant(cfg);
         if (!var) return GEMM_ERR_INTERNAL;
     }
@@ -464,7 +474,7 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
     gemm_tile_config ucfg = cfg;
     const Variant* uvar = var;
     if (cfg.staging != 7) {
-        ucfg = heuristic(M, N, b_layout, false);
+        ucfg = heuristic(M, N, K, b_layout, false);
         uvar = find_variant(ucfg);
         if (!uvar) return GEMM_ERR_INTERNAL;
     }

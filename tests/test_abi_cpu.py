@@ -227,7 +227,8 @@ def test_misaligned_rows_plan_the_register_staged_mfma_path(L):
         spg.gemm_destroy(h)
         aligned = K % 8 == 0 and (layout == "nk" or N % 8 == 0)
         assert c.block_k == 64 and (c.staging == 7) != aligned, (M, N, K, layout, c)
-        assert c.mfma == 32
+        # mode 7 runs 32x32x16 MFMAs; the aligned plans are the 8-wave 16x16x32 tiles
+        assert c.mfma == (32 if c.staging == 7 else 16)
     h = spg.gemm_create(100, 101, 64, "bf16", "bf16", "nk")   # [N,K] rows are 16-B
     assert spg.gemm_get_config(h).block_k == 64 and spg.gemm_get_config(h).staging != 7
     spg.gemm_destroy(h)
@@ -303,9 +304,15 @@ def test_heuristic_tiles(L):
     assert (tn.block_m, tn.block_n, tn.mfma, tn.staging, tn.schedule) == (256, 256, 16, 6, 2)
     one_round = cfg(4096, 4096, 4096)
     assert (one_round.staging, one_round.schedule) == (0, 0)
-    assert cfg(1024, 8192, 8192).mfma == 16 and cfg(256, 256, 256).mfma == 32
+    assert cfg(1024, 8192, 8192).mfma == 16
+    # small problems: 128x128, 8 waves of 32x64, 16x16x32; a two-slot ring for few
+    # k-tiles or two rounds and more, three slots for one round with more than 16
     small = cfg(256, 256, 256)
-    assert (small.block_m, small.block_n) == (128, 128)
+    assert (small.block_m, small.block_n, small.wave_m, small.wave_n, small.mfma, small.stages) == \
+        (128, 128, 32, 64, 16, 2)
+    assert cfg(2048, 2048, 2048).stages == 3      # 256 tiles, 32 k-tiles
+    assert cfg(2048, 2048, 1024).stages == 2      # 16 k-tiles
+    assert cfg(1024, 2048, 4096).stages == 3      # 128 tiles, 64 k-tiles
     # the cost model: rounds of 256 CUs x tile area / per-tile throughput
     shard = cfg(1024, 8192, 8192)           # 128 tiles of 256x256, 256 of 256x128
     assert (shard.block_m, shard.block_n) == (256, 128)

@@ -304,8 +304,8 @@ def test_misaligned_mode_copies(b_nk, tile):
 
 
 @pytest.mark.parametrize("b_nk", [False, True], ids=["kn", "nk"])
-@pytest.mark.parametrize("tile", [(256, 256, 8), (192, 256, 8), (128, 128, 4)],
-                         ids=["256x256w8", "192x256w8", "128x128w4"])
+@pytest.mark.parametrize("tile", [(256, 256, 8), (192, 256, 8), (128, 128, 4), (128, 128, 8)],
+                         ids=["256x256w8", "192x256w8", "128x128w4", "128x128w8"])
 def test_direct_mode_copies(b_nk, tile):
     # the direct-to-LDS modes: rows 16 bytes apart (K % 8 == 0; N % 8 == 0 for [K,N])
     t = Tile(*tile)
