@@ -26,7 +26,7 @@ POISON_OUT = os.path.join(HERE, "libspgemm_poison.so")
 # (S = 2..5 with 32x32x16, the 16x16x32 tiles, the A-deep and B-deep rings, release
 # delay 1, persistent tiles), the wave-specialized ring and the register-staged
 # misaligned mode, which also covers every configuration the shape heuristic picks.
-POISON_UNITS = (8, 14, 21, 23, 24, 25, 26, 27, 28, 30, 31, 32, 33, 34)
+POISON_UNITS = (8, 14, 21, 23, 24, 25, 26, 27, 28, 29, 30, 31, 32, 33, 34, 35)
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in any generated code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

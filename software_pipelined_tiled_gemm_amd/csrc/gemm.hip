@@ -268,9 +268,19 @@ gemm_tile_config heuristic(int64_t M, int64_t N, int64_t K, gemm_b_layout bl, bo
     // 2048^3 19.3 against 23.4; but 256^3 4.4 against 5.1 us, 1024^3 8.7 against 9.5,
     // 2048x4096x4096 (512 tiles) 65.7 against 70.6, 8192^3 925 against 958.
     int st = best->st;
+    const int64_t nk = (K + best->bk - 1) / best->bk;
     if (best->bm == 128 && best->bn == 128)
-        st = (tiles < 2 * cus && (K + best->bk - 1) / best->bk > 16) ? 3 : 2;
-    if (!v) v = find_cfg(best->bm, best->bn, best->bk, st, 0, best->wm, best->wn, 0, best->mfma);
+        st = (tiles < 2 * cus && nk > 16) ? 3 : 2;
+    // Schedule of the two-slot / three-slot rings: compiler-placed (with its interleaving
+    // hint) for 256x128 and for 256x256 with more than 16 k-tiles, hand-placed otherwise.
+    // Measured interleaved against the hand-placed schedule with a control copy:
+    // 1024x8192x8192 (256x128) bf16 NN -2.6%, fp16 TN -1.3%; 4096^3 (256x256, one round)
+    // fp16 TN -2.1%, bf16 NN -1.3%; but 3000x5000x1000 (16 k-tiles) +0.8%, 192x256 even,
+    // and the 128x128 tile +0.5 .. +6% (2048^3).
+    int sched = 0;
+    if ((best->bm == 256 && best->bn == 128) || (best->bm == 256 && best->bn == 256 && nk > 16))
+        sched = 1;
+    if (!v) v = find_cfg(best->bm, best->bn, best->bk, st, 0, best->wm, best->wn, 0, best->mfma, sched);
     gemm_tile_config c = v->cfg;
     // 4 tile rows per raster group: with the 16x16x32 tiles at 8192^3 (32 tile rows),
     // measured interleaved: group_m 2 / 4 / 8 / 16 / 32 = 758 / 730 / 740 / 752 / 911 us

@@ -302,8 +302,11 @@ def test_heuristic_tiles(L):
     spg.gemm_destroy(h)
     # B stored [N,K] on a grid of several rounds: the same ring under the ping-pong schedule
     assert (tn.block_m, tn.block_n, tn.mfma, tn.staging, tn.schedule) == (256, 256, 16, 6, 2)
+    # one round of 256x256 tiles: the two-slot ring, compiler-placed with more than 16
+    # k-tiles, hand-placed with fewer
     one_round = cfg(4096, 4096, 4096)
-    assert (one_round.staging, one_round.schedule) == (0, 0)
+    assert (one_round.staging, one_round.schedule) == (0, 1)
+    assert cfg(4096, 4096, 1024).schedule == 0
     assert cfg(1024, 8192, 8192).mfma == 16
     # small problems: 128x128, 8 waves of 32x64, 16x16x32; a two-slot ring for few
     # k-tiles or two rounds and more, three slots for one round with more than 16
@@ -315,7 +318,7 @@ def test_heuristic_tiles(L):
     assert cfg(1024, 2048, 4096).stages == 3      # 128 tiles, 64 k-tiles
     # the cost model: rounds of 256 CUs x tile area / per-tile throughput
     shard = cfg(1024, 8192, 8192)           # 128 tiles of 256x256, 256 of 256x128
-    assert (shard.block_m, shard.block_n) == (256, 128)
+    assert (shard.block_m, shard.block_n, shard.schedule) == (256, 128, 1)
     gelu = cfg(3072, 4096, 4096)            # 192 tiles of 256x256, 256 of 192x256: one round
     assert (gelu.block_m, gelu.block_n, gelu.wave_m, gelu.mfma) == (192, 256, 96, 16)
     tall = cfg(6144, 8192, 8192)            # 3 rounds of 256x256 against 4 of 192x256
