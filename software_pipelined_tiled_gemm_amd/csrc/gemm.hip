@@ -229,27 +229,33 @@ gemm_tile_config heuristic(int64_t M, int64_t N, int64_t K, gemm_b_layout bl, bo
     const Cand ucands[] = {{256, 256, 64, 2, 128, 64, 32, 1.0},
                            {256, 128, 64, 3, 128, 64, 32, 0.85},
                            {128, 128, 64, 3, 64, 64, 32, 0.66}};
+    // Only candidates the library holds compete (a build may compile a subset of
+    // variants.inc); with none, the zero configuration returned matches no variant.
     if (!aligned) {
-        const Cand* ub = nullptr;
+        const Variant* ub = nullptr;
         double ub_t = 0.0;
         for (const Cand& c : ucands) {
+            const Variant* v = find_cfg(c.bm, c.bn, c.bk, c.st, 7, c.wm, c.wn, 0, c.mfma);
+            if (!v) continue;
             const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
             const double t = (double)((tiles + cus - 1) / cus) * c.bm * c.bn / c.eff;
-            if (!ub || t < ub_t) { ub = &c; ub_t = t; }
+            if (!ub || t < ub_t) { ub = v; ub_t = t; }
         }
-        gemm_tile_config c = find_cfg(ub->bm, ub->bn, ub->bk, ub->st, 7, ub->wm, ub->wn, 0, ub->mfma)->cfg;
+        if (!ub) return gemm_tile_config{};
+        gemm_tile_config c = ub->cfg;
         c.group_m = kDefaultGroupM;
         c.xcd_remap = 1;
         return c;
     }
-    (void)bl;
     const Cand* best = nullptr;
     double best_t = 0.0;
     for (const Cand& c : cands) {
+        if (!find_cfg(c.bm, c.bn, c.bk, c.st, 0, c.wm, c.wn, 0, c.mfma)) continue;
         const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
         const double t = (double)((tiles + cus - 1) / cus) * c.bm * c.bn / c.eff;
         if (!best || t < best_t) { best = &c; best_t = t; }
     }
+    if (!best) return gemm_tile_config{};
     // Grids of two rounds or more on the 256x256 tile: the B-deep ring (staging 6, three
     // B slots).  With B stored [K,N] under the compiler-placed schedule: a [K,N] k-tile
     // of B is 64 rows 2*N bytes apart, and its copies are the ones that land late
@@ -281,6 +287,8 @@ gemm_tile_config heuristic(int64_t M, int64_t N, int64_t K, gemm_b_layout bl, bo
     if ((best->bm == 256 && best->bn == 128) || (best->bm == 256 && best->bn == 256 && nk > 16))
         sched = 1;
     if (!v) v = find_cfg(best->bm, best->bn, best->bk, st, 0, best->wm, best->wn, 0, best->mfma, sched);
+    // (the candidate's own two-slot / three-slot ring, compiled: checked above)
+    if (!v) v = find_cfg(best->bm, best->bn, best->bk, best->st, 0, best->wm, best->wn, 0, best->mfma);
     gemm_tile_config c = v->cfg;
     // 4 tile rows per raster group: with the 16x16x32 tiles at 8192^3 (32 tile rows),
     // measured interleaved: group_m 2 / 4 / 8 / 16 / 32 = 758 / 730 / 740 / 752 / 911 us
@@ -484,9 +492,10 @@ gemm_status gemm_create(gemm_handle* out, int64_t M, int64_t N, int64_t K, gemm_
     gemm_tile_config ucfg = cfg;
     const Variant* uvar = var;
     if (cfg.staging != 7) {
+        // (a library without copy mode 7 plans no twin: misaligned pointers then take the
+        // simple kernel)
         ucfg = heuristic(M, N, K, b_layout, false);
         uvar = find_variant(ucfg);
-        if (!uvar) return GEMM_ERR_INTERNAL;
     }
     gemm_plan* p = new (std::nothrow) gemm_plan;
     if (!p) return GEMM_ERR_OUT_OF_MEMORY;

@@ -61,6 +61,38 @@ def test_poison_library_exports_the_same_abi():
     assert 0 < len(poison) < len(prod) and set(poison) <= prod
 
 
+def _plan(lib, M, N, K, dt, lay):
+    h = ctypes.c_void_p()
+    st = lib.gemm_create(ctypes.byref(h), M, N, K, spg.DTYPES[dt], spg.DTYPES[dt],
+                         spg.B_LAYOUTS[lay], spg.EPILOGUES["none"], None)
+    assert st == 0, (M, N, K, dt, lay, st)
+    c = spg.TileConfig()
+    assert lib.gemm_get_config(h, ctypes.byref(c)) == 0
+    twin = spg.TileConfig()
+    # a pointer that is not 16-byte aligned: the plan's misaligned-operand twin
+    assert lib.gemm_launch_config(h, ctypes.c_void_p(2), ctypes.c_void_p(0), ctypes.c_void_p(0),
+                                  ctypes.byref(twin)) == 0
+    lib.gemm_destroy(h)
+    return c.as_dict(), twin.as_dict()
+
+
+def test_poison_library_plans_what_the_production_library_plans():
+    # The poison build compiles a subset of the configurations; the heuristic considers
+    # only the ones a library holds, so the poison build tests the production plans only
+    # if it holds every configuration the heuristic picks (and every misaligned twin).
+    if not os.path.exists(spg.POISON_LIB_PATH):
+        pytest.fail("libspgemm_poison.so is not built; run __graft_entry__.build()")
+    P, Q = spg.poison_lib(), spg.lib()
+    shapes = [(8192, 8192, 8192), (6144, 6144, 6144), (4096, 4096, 4096), (4096, 4096, 1024),
+              (3072, 4096, 4096), (3000, 5000, 1000), (3000, 5000, 1001), (1024, 8192, 8192),
+              (2048, 2048, 2048), (2048, 2048, 1024), (1024, 2048, 4096), (1024, 1024, 1024),
+              (256, 256, 256), (300, 263, 200), (16384, 1024, 1024), (512, 512, 8192), (129, 8, 64)]
+    for (M, N, K) in shapes:
+        for dt in ("f16", "bf16"):
+            for lay in ("kn", "nk"):
+                assert _plan(P, M, N, K, dt, lay) == _plan(Q, M, N, K, dt, lay), (M, N, K, dt, lay)
+
+
 def test_status_strings(L):
     for code, text in spg.STATUS.items():
         assert spg.gemm_status_string(code) == text
