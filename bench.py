@@ -605,9 +605,22 @@ GELU_ABLATIONS = [
     ("256x256x64, 32x32x16 (192 tiles)", "256x256x64:2:1:4:0:128x64:1:0"),
     ("256x128x64, S=3, 8 waves of 64x64, 16x16x32 (384 tiles: 1.5 rounds)", "256x128x64:3:1:4:0:64x64:1:0:0:0:1:16"),
     ("128x128x64, S=3, 4 waves of 64x64, 32x32x16 (768 tiles: 3 rounds)", "128x128x64:3:1:4:0:64x64:1:0"),
+    ("128x128x64, S=2, 8 waves of 32x64, 16x16x32 (768 tiles: 3 rounds)", "128x128x64:2:1:4:0:32x64:1:0:0:0:1:16"),
 ]
 
-ABLATIONS_BY_WORKLOAD = {"nn_bf16_3072x4096x4096_gelu": GELU_ABLATIONS}
+# The small-problem tile at the matmul + ReLU workload (2048x2048x1024 -> fp32): one round
+# of 256 tiles of 128x128, or fewer, larger tiles
+RELU_ABLATIONS = [
+    ("default: 128x128x64, S=3, 8 waves of 32x64, 16x16x32 (256 tiles; 96 KiB: one workgroup per CU)", "128x128x64:3:1:4:0:32x64:1:0:0:0:1:16"),
+    ("the same with S=2 (64 KiB: two workgroups can share a CU)", "128x128x64:2:1:4:0:32x64:1:0:0:0:1:16"),
+    ("128x128x64, S=3, 4 waves of 64x64, 32x32x16 (the previous small-problem tile)", "128x128x64:3:1:4:0:64x64:1:0"),
+    ("128x128x64, S=2, 4 waves of 64x64, 32x32x16", "128x128x64:2:1:4:0:64x64:1:0"),
+    ("256x128x64, S=3, 8 waves of 64x64, 16x16x32, compiler-placed (128 tiles)", "256x128x64:3:1:4:0:64x64:1:1:0:0:1:16"),
+    ("256x256x64, S=2, 8 waves of 128x64, 16x16x32 (64 tiles)", "256x256x64:2:1:4:0:128x64:1:0:0:0:1:16"),
+]
+
+ABLATIONS_BY_WORKLOAD = {"nn_bf16_3072x4096x4096_gelu": GELU_ABLATIONS,
+                         "nn_f16_2048x2048x1024_relu_f32out": RELU_ABLATIONS}
 
 
 def ablations_for(workload):
@@ -615,11 +628,14 @@ def ablations_for(workload):
     return ABLATIONS_BY_WORKLOAD.get(workload, ABLATIONS)
 
 
-def run_ablations(w, steps, warmup):
+def run_ablations(w, steps, warmup, min_warmup_s):
     rows = []
     for label, spec in ablations_for(w.name):
         cfg = parse_tile(spec)
-        t, used = time_gemm(w, steps, warmup, cfg)
+        # every row gets the same warm-up as the benchmark lines (at least min_warmup_s of
+        # back-to-back launches, out of the clock ramp); kernels shorter than a host launch
+        # are timed as launches captured in a HIP graph
+        t, used = time_gemm(w, steps, warmup, cfg, min_warmup_s, graph=w.flops < 2e10)
         k = t["mean_ms"]
         rows.append({"label": label, "tile": spec, "kernel_us": round(k * 1e3, 2),
                      "kernel_us_median": round(t["median_ms"] * 1e3, 2),
@@ -670,7 +686,7 @@ def main():
     w = W.WORKLOADS[args.workload]
     log(f"bench: {w.describe()}")
     if args.ablations:
-        run_ablations(w, args.steps, args.warmup)
+        run_ablations(w, args.steps, args.warmup, args.min_warmup_s)
         return
     force = parse_tile(args.tile) if args.tile else None
     t, cfg = time_gemm(w, args.steps, args.warmup, force, args.min_warmup_s)

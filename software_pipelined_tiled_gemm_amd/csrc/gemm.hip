@@ -269,14 +269,17 @@ gemm_tile_config heuristic(int64_t M, int64_t N, int64_t K, gemm_b_layout bl, bo
     if (best->bm == 256 && best->bn == 256 && tiles >= 2 * cus)
         v = find_cfg(256, 256, 64, 2, 6, best->wm, best->wn, 0, 16, bl == GEMM_B_KN ? 1 : 2);
     // 128x128: S = 3 (96 KiB: one workgroup per CU) on grids of less than two rounds
-    // with more than 16 k-tiles, else S = 2 (64 KiB: two workgroups share a CU).
+    // with more than 16 k-tiles or at least half a round of tiles, else S = 2 (64 KiB:
+    // two workgroups can share a CU).  On a grid of about one round, S = 2 lets the
+    // dispatcher put two workgroups on one CU, which then sets the kernel time.
     // Measured: 1024x2048x4096 (128 tiles) 24.9 us with S = 3 against 39.6 with S = 2,
-    // 2048^3 19.3 against 23.4; but 256^3 4.4 against 5.1 us, 1024^3 8.7 against 9.5,
-    // 2048x4096x4096 (512 tiles) 65.7 against 70.6, 8192^3 925 against 958.
+    // 2048^3 19.3 against 23.4, 2048x2048x1024 (256 tiles, 16 k-tiles) 14.4 against
+    // 14.4 .. 16.2 from run to run; but 256^3 4.4 against 5.1 us, 1024^3 (64 tiles) 8.7
+    // against 9.5, 2048x4096x4096 (512 tiles) 65.7 against 70.6, 8192^3 925 against 958.
     int st = best->st;
     const int64_t nk = (K + best->bk - 1) / best->bk;
     if (best->bm == 128 && best->bn == 128)
-        st = (tiles < 2 * cus && nk > 16) ? 3 : 2;
+        st = (tiles < 2 * cus && (nk > 16 || 2 * tiles >= cus)) ? 3 : 2;
     // Schedule of the two-slot / three-slot rings: compiler-placed (with its interleaving
     // hint) for 256x128 and for 256x256 with more than 16 k-tiles, hand-placed otherwise.
     // Measured interleaved against the hand-placed schedule with a control copy:

@@ -340,13 +340,14 @@ def test_heuristic_tiles(L):
     assert (one_round.staging, one_round.schedule) == (0, 1)
     assert cfg(4096, 4096, 1024).schedule == 0
     assert cfg(1024, 8192, 8192).mfma == 16
-    # small problems: 128x128, 8 waves of 32x64, 16x16x32; a two-slot ring for few
-    # k-tiles or two rounds and more, three slots for one round with more than 16
+    # small problems: 128x128, 8 waves of 32x64, 16x16x32; three slots on grids under
+    # two rounds with more than 16 k-tiles or at least half a round of tiles, else two
     small = cfg(256, 256, 256)
     assert (small.block_m, small.block_n, small.wave_m, small.wave_n, small.mfma, small.stages) == \
         (128, 128, 32, 64, 16, 2)
     assert cfg(2048, 2048, 2048).stages == 3      # 256 tiles, 32 k-tiles
-    assert cfg(2048, 2048, 1024).stages == 2      # 16 k-tiles
+    assert cfg(2048, 2048, 1024).stages == 3      # 16 k-tiles, but a full round of tiles
+    assert cfg(1024, 1024, 1024).stages == 2      # 64 tiles, 16 k-tiles
     assert cfg(1024, 2048, 4096).stages == 3      # 128 tiles, 64 k-tiles
     # the cost model: rounds of 256 CUs x tile area / per-tile throughput
     shard = cfg(1024, 8192, 8192)           # 128 tiles of 256x256, 256 of 256x128
